@@ -1,0 +1,148 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module draws the inputs that both the HIP path and the CPU oracle receive.
+It holds none of the attention arithmetic: only random draws, the block-mask
+pattern and round-to-nearest-even conversion to bf16 storage.  It imports
+numpy only, so tests and the oracle's callers can use it without the GPU
+library.
+
+The five workloads stand in for the shapes the FlashAttention reading guide
+(xyznot.com/tr/paper/2205.14135, "Sonuçlar") reports on, without their data:
+
+  tiny      B=1  H=2  N=128   d=64   fp32  dense          exact fp32 check
+  gpt2      B=8  H=12 N=1024  d=64   bf16  causal         GPT-2-small attention
+  long      B=2  H=16 N=4096  d=128  bf16  causal         1% of K rows x20
+  sparse    B=4  H=8  N=8192  d=64   bf16  128-tile block mask, Bernoulli(0.25)
+                                           keep pattern plus the diagonal
+  verylong  B=1  H=8  N=16384 d=128  bf16  causal         sigma = 0.5
+
+Recipe (the same for every workload): ``rng = numpy.random.default_rng(seed)``
+(PCG64); draw Q, K, V, dO in that order, each
+``rng.standard_normal((B, H, N, d), dtype=float32) * sigma``; then, for
+``long``, choose floor(0.01 * B*H*N) rows of the flattened [B*H*N] K row index
+without replacement and multiply those rows by 20; then, for ``sparse``, draw
+the [T, T] keep pattern (T = ceil(N/128)) as ``rng.random((T, T)) < 0.25`` and
+set its diagonal.  The scale is 1/sqrt(d).  bf16 workloads are rounded to bf16
+(round to nearest, ties to even) after all draws; the rounded values are the
+inputs of both sides.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, replace
+from typing import Optional
+
+import numpy as np
+
+MASK_BLOCK = 128
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str              # "bf16" or "fp32"
+    causal: bool
+    sigma: float = 1.0
+    k_row_frac: float = 0.0  # fraction of K rows scaled by k_row_gain
+    k_row_gain: float = 1.0
+    mask_density: Optional[float] = None   # Bernoulli keep probability
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def tiles(self) -> int:
+        return -(-self.N // MASK_BLOCK)
+
+    def with_shape(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 2, 128, 64, "fp32", False, seed=1001),
+    "gpt2": Workload("gpt2", 8, 12, 1024, 64, "bf16", True, seed=1002),
+    "long": Workload("long", 2, 16, 4096, 128, "bf16", True,
+                     k_row_frac=0.01, k_row_gain=20.0, seed=1003),
+    "sparse": Workload("sparse", 4, 8, 8192, 64, "bf16", False,
+                       mask_density=0.25, seed=1004),
+    "verylong": Workload("verylong", 1, 8, 16384, 128, "bf16", True,
+                         sigma=0.5, seed=1005),
+}
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16 (ties to even); returns float32
+    holding exactly representable bf16 values.  Inputs must be finite."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32).astype(np.uint64)
+    bias = 0x7FFF + ((bits >> 16) & 1)
+    bits = ((bits + bias) & 0xFFFF0000).astype(np.uint32)
+    return bits.view(np.float32)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """The uint16 bf16 encoding of float32 values that are already bf16."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def make_block_mask(rng: np.random.Generator, tiles: int, density: float) -> np.ndarray:
+    """[T, T] uint8 keep pattern: Bernoulli(density) with the diagonal set."""
+    keep = rng.random((tiles, tiles)) < density
+    keep[np.arange(tiles), np.arange(tiles)] = True
+    return keep.astype(np.uint8)
+
+
+def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
+    """Draw the inputs of workload ``w``.
+
+    Returns dict(q, k, v, do: float32 [B,H,N,d] holding the storage-type
+    values, mask: uint8 [T,T] or None, scale, causal, dtype).
+    """
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    shape = (w.B, w.H, w.N, w.d)
+    q = rng.standard_normal(shape, dtype=np.float32) * np.float32(w.sigma)
+    k = rng.standard_normal(shape, dtype=np.float32) * np.float32(w.sigma)
+    v = rng.standard_normal(shape, dtype=np.float32) * np.float32(w.sigma)
+    do = rng.standard_normal(shape, dtype=np.float32) * np.float32(w.sigma)
+    if w.k_row_frac > 0.0:
+        rows_total = w.B * w.H * w.N
+        count = int(math.floor(w.k_row_frac * rows_total))
+        idx = rng.choice(rows_total, size=count, replace=False)
+        flat = k.reshape(rows_total, w.d)
+        flat[idx] *= np.float32(w.k_row_gain)
+    mask = None
+    if w.mask_density is not None:
+        mask = make_block_mask(rng, w.tiles, w.mask_density)
+    if w.dtype == "bf16":
+        q, k, v, do = (bf16_round(t) for t in (q, k, v, do))
+    return dict(q=q, k=k, v=v, do=do, mask=mask, scale=w.scale,
+                causal=w.causal, dtype=w.dtype)
+
+
+def random_inputs(B, H, N, d, dtype="bf16", seed=0, sigma=1.0):
+    """Plain iid N(0, sigma^2) Q, K, V, dO of any shape (edge-case tests)."""
+    rng = np.random.default_rng(seed)
+    shape = (B, H, N, d)
+    ts = [rng.standard_normal(shape, dtype=np.float32) * np.float32(sigma)
+          for _ in range(4)]
+    if dtype == "bf16":
+        ts = [bf16_round(t) for t in ts]
+    return dict(zip(("q", "k", "v", "do"), ts))
+
+
+def random_block_mask(N: int, density: float, seed: int, keep_diag=True) -> np.ndarray:
+    """Seeded [ceil(N/128)]^2 uint8 block mask (for edge-case tests)."""
+    rng = np.random.default_rng(seed)
+    t = -(-N // MASK_BLOCK)
+    keep = rng.random((t, t)) < density
+    if keep_diag:
+        keep[np.arange(t), np.arange(t)] = True
+    return keep.astype(np.uint8)
