@@ -1,0 +1,226 @@
+"""Benchmark: exact-attention forward + training backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long]
+
+A step is one pass of the whole hot path over one batch: fa_fwd, then the
+three backward phases (D preprocess, dK/dV pass, dQ pass), on torch's current
+stream, inputs resident in HBM.  W untimed warm-up steps, then exactly K timed
+steps bracketed by torch.cuda.synchronize(); each kernel is also bracketed by
+HIP events on the same stream for per-kernel durations.  Prints ONE JSON line.
+
+Workloads are seeded synthetic inputs with the shapes of the FlashAttention
+reading guide's training workloads (io_aware_exact_09_amd/workloads.py); the
+default, "long" (B=2, H=16, N=4096, d=128, bf16, causal), is the N >= 4096,
+d = 128 shape the throughput target is stated for.
+
+Throughput uses algorithmic FLOPs (4 d per kept pair forward, 10 d backward;
+causal and block-sparse skipping excluded, the dQ pass's recomputation not
+counted).  The roofline object is for the kernel with the largest share of the
+step; peak is the published MI355X dense bf16 MFMA rate, 2.5 PFLOP/s (fp32
+MFMA 157.3 TFLOP/s for fp32 workloads).
+
+The cpu_baseline leg times the CPU fp64 oracle on a bounded sample of the same
+workload (whole heads, about 10-30 s) on this host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target duration of the CPU oracle sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, x, budget_s):
+    """Time the fp64 oracle (fwd + bwd, whole heads) on a bounded sample."""
+    import oracle
+    from io_aware_exact_09_amd import accounting
+    try:
+        import threadpoolctl
+        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()),
+                      default=os.cpu_count())
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = 0
+    t0 = time.perf_counter()
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        oracle.forward_backward(x["q"][sl], x["k"][sl], x["v"][sl], x["do"][sl], w.scale,
+                                w.causal, x["mask"])
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    f = accounting.flops(1, done, w.N, w.d, w.causal, x["mask"])
+    return {
+        "value": (f["fwd"] + f["bwd"]) / el / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {len(heads)} heads (fwd+bwd, fp64 NumPy, S and P materialised), "
+                  f"{el:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
+              "(heads are independent, so several GPUs would each run this same "
+              "single-GPU step on their share).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from io_aware_exact_09_amd import accounting, fa
+    from io_aware_exact_09_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = W.WORKLOADS[args.workload]
+    x = W.make_inputs(w)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v, do = (torch.from_numpy(x[n]).to(dev).to(tdt).contiguous()
+                   for n in ("q", "k", "v", "do"))
+    mask = None if x["mask"] is None else torch.from_numpy(x["mask"]).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8,
+                     device=dev)
+    sc, cz = w.scale, w.causal
+
+    phases = ["fwd", "pre", "dkdv", "dq"]
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        fa.fa_fwd(q, k, v, o, lse, sc, cz, mask)
+        if ev: ev[1].record()
+        fa.fa_bwd_preprocess(o, do, ws)
+        if ev: ev[2].record()
+        fa.fa_bwd_dkdv(q, k, v, do, lse, dk, dv, sc, cz, mask, ws)
+        if ev: ev[3].record()
+        fa.fa_bwd_dq(q, k, v, do, lse, dq, sc, cz, mask, ws)
+        if ev: ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = {p: [e[i].elapsed_time(e[i + 1]) for e in evs] for i, p in enumerate(phases)}
+    steps_ms = [e[0].elapsed_time(e[4]) for e in evs]
+    span_ms = evs[0][0].elapsed_time(evs[-1][4])
+    ms_step = span_ms / args.steps
+    fl = accounting.flops(w.B, w.H, w.N, w.d, w.causal, x["mask"])
+    elem = 2 if w.dtype == "bf16" else 4
+    hb = accounting.hbm_bytes(w.B, w.H, w.N, w.d, elem)
+    peak = PEAK_TFLOPS[w.dtype]
+    total = fl["fwd"] + fl["bwd"]
+    value = total / (ms_step * 1e-3) / 1e12
+
+    avg = {p: statistics.mean(per[p]) for p in phases}
+    kflops = {"fwd": fl["fwd_kernel"], "dkdv": fl["dkdv_kernel"], "dq": fl["dq_kernel"]}
+    names = {"fwd": "fa_fwd_kernel", "pre": "fa_bwd_delta_kernel", "dkdv": "fa_bwd_dkdv_kernel",
+             "dq": "fa_bwd_dq_kernel"}
+    dom = max(phases, key=lambda p: avg[p])
+    if dom == "pre":
+        ach = hb["pre_kernel"] / (avg[dom] * 1e-3) / 1e9
+        roof = {"kernel": names[dom], "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None}
+    else:
+        ach = kflops[dom] / (avg[dom] * 1e-3) / 1e12
+        roof = {"kernel": names[dom], "bound": "mfma", "achieved": ach, "peak": peak,
+                "unit": "TFLOP/s", "frac": ach / peak, "traffic": None,
+                "algorithmic_flops_per_launch": kflops[dom], "avg_launch_ms": avg[dom]}
+
+    kernels = {}
+    for p in phases:
+        entry = {"avg_ms": avg[p], "median_ms": statistics.median(per[p])}
+        if p in kflops:
+            entry["tflops"] = kflops[p] / (avg[p] * 1e-3) / 1e12
+        else:
+            entry["gbs"] = hb["pre_kernel"] / (avg[p] * 1e-3) / 1e9
+        kernels[names[p]] = entry
+
+    fwd_ms = avg["fwd"]
+    bwd_ms = avg["pre"] + avg["dkdv"] + avg["dq"]
+    s = sorted(steps_ms)
+    n = len(s)
+    mean = statistics.mean(s)
+    sd = statistics.stdev(s) if n > 1 else 0.0
+    # two-sided 95% Student t critical values for small samples, else normal
+    tcrit = {2: 12.706, 3: 4.303, 4: 3.182, 5: 2.776, 6: 2.571, 8: 2.365, 10: 2.262,
+             15: 2.145, 20: 2.093, 30: 2.045}.get(n, 1.96 if n > 30 else 2.1)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(w, x, args.cpu_seconds)
+
+    out = {
+        "metric": "attention fwd+bwd TFLOP/s (bf16, 1 MI355X) and % of MFMA peak",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded iid normal Q, K, V, dO)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "block_sparse": x["mask"] is not None,
+                   "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)"},
+        "pct_of_peak": 100.0 * value / peak,
+        "fwd_tflops": fl["fwd"] / (fwd_ms * 1e-3) / 1e12,
+        "bwd_tflops": fl["bwd"] / (bwd_ms * 1e-3) / 1e12,
+        "fwd_ms": fwd_ms,
+        "bwd_ms": bwd_ms,
+        "step_ms_stats": {"mean": mean, "p50": s[n // 2], "p95": s[min(n - 1, int(0.95 * n))],
+                          "ci95_half_width": tcrit * sd / math.sqrt(n) if n > 1 else None},
+        "wall_s_timed": wall,
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "peak_tflops": peak,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

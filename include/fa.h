@@ -1,0 +1,163 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library (libfa.so).
+ *
+ * The library computes exact attention O = softmax(scale * Q K^T) V and its
+ * training gradients without ever writing the N x N score or probability
+ * matrices to device memory: the forward walks key/value tiles with running
+ * (row max, row sum) statistics, and the backward recomputes the scores tile by
+ * tile from Q, K, V and the saved per-row log-sum-exp.
+ *
+ * Pages this interface follows:
+ *   [Training-FA] "Как работает FlashAttention для training (не только
+ *                 inference)?" -- aivaro.ru/en/answers/474
+ *   [Week-13]     "Неделя 13. GPU и FlashAttention" --
+ *                 snula.amonoc.com/course/ru/week-13.html
+ *   [FA-guide]    "FlashAttention: IO Farkındalığı ile Hızlı ve Bellek
+ *                 Açısından Verimli Tam Dikkat" (reading guide to arXiv
+ *                 2205.14135) -- xyznot.com/tr/paper/2205.14135
+ *
+ * Common conventions for every entry point
+ * ----------------------------------------
+ *  - Tensors are DEVICE pointers owned by the caller.  The library never
+ *    allocates, frees or synchronises; every kernel is enqueued on `stream`
+ *    (a hipStream_t; NULL means the default stream) and the call returns
+ *    without waiting.
+ *  - Q, K, V, O, dO, dQ, dK, dV: [B, H, N, d] contiguous row-major, all of the
+ *    same element type `dtype`; 16-byte aligned base pointers.
+ *  - LSE: [B, H, N] fp32, natural-log log-sum-exp of each query row's scaled
+ *    scores; 4-byte aligned.  -inf for a row that keeps no key.
+ *  - block_mask: NULL (dense) or a device array uint8[T][T], T = ceil(N/128),
+ *    row-major; entry [i][j] != 0 keeps the 128 x 128 tile of query rows
+ *    128i..128i+127 and key rows 128j..128j+127.  One mask is shared by every
+ *    (batch, head).  With causal != 0 both restrictions apply.
+ *  - causal != 0 keeps key j for query i only when j <= i (self-attention,
+ *    N queries against N keys).
+ *  - d must be 64 or 128; N >= 1 (any N: the last tile is masked by bounds);
+ *    B, H >= 1; N * d and B * H * ceil(N/128) must fit in int32.
+ *  - scale must be finite and >= 0 (1/sqrt(d) is the usual value).
+ *  - Outputs must not overlap inputs or each other.
+ *  - Validation runs before anything is enqueued; on any error nothing is
+ *    written and no kernel is launched.  A launch failure is reported as
+ *    FA_ERR_LAUNCH; faults inside a kernel surface, as usual for HIP, at the
+ *    caller's next synchronisation.  No C++ exception crosses this interface.
+ *  - Calls are stateless and reentrant; results are deterministic (no atomics:
+ *    every output element is written by exactly one work-group).
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,       /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,      /* B, H or N < 1, or a size overflows int32 */
+  FA_ERR_HEAD_DIM = 3,   /* d not in {64, 128} */
+  FA_ERR_DTYPE = 4,      /* dtype not an fa_dtype value */
+  FA_ERR_ALIGN = 5,      /* a tensor pointer is misaligned */
+  FA_ERR_WORKSPACE = 6,  /* workspace NULL, misaligned or too small */
+  FA_ERR_LAUNCH = 7,     /* the HIP runtime refused a kernel launch */
+  FA_ERR_ARG = 8,        /* scale not finite or negative */
+  FA_ERR_ALIAS = 9       /* an output overlaps an input or another output */
+} fa_status;
+
+typedef enum { FA_BF16 = 0, FA_FP32 = 1 } fa_dtype;
+
+#define FA_MASK_BLOCK 128
+
+/*
+ * fa_fwd -- exact attention forward.
+ *
+ * Computes, for every (b, h) and query row i,
+ *   O_i   = sum_j P_ij V_j,  P_ij = exp(s_ij - LSE_i) over kept keys j,
+ *   LSE_i = ln sum_{kept j} exp(s_ij),  s_ij = scale * <Q_i, K_j>,
+ * tile by tile with running row max and row sum, so S and P stay on chip
+ * ([Training-FA] §2.1; [FA-guide] "Yöntem" steps 1-4 and the two-part rule of
+ * "Artımsal Softmax Takibi"; [Week-13] Step 2).  Only O and the per-row
+ * log-sum-exp are written ([Week-13] Step 2 keeps the logsumexp for the
+ * backward).  Arithmetic: bf16 (or fp32) operands, fp32 accumulation and
+ * statistics; P is rounded to the operand type before the P V product.
+ * A row with no kept key gets O_i = 0 and LSE_i = -inf.
+ *
+ *   Q, K, V   in : [B,H,N,d] dtype
+ *   O         out: [B,H,N,d] dtype (overwritten)
+ *   LSE       out: [B,H,N] fp32 (overwritten)
+ */
+fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                 int B, int H, int N, int d, float scale, int causal,
+                 const unsigned char* block_mask, fa_dtype dtype, void* stream);
+
+/*
+ * fa_bwd_workspace_bytes -- size of the scratch buffer fa_bwd needs: one fp32
+ * per query row (D_i = sum_k dO_ik O_ik), i.e. 4 * B * H * N bytes, so the
+ * backward's extra memory is O(N) ([FA-guide] "Karmaşıklık Analizi").
+ * Returns 0 for sizes that fa_bwd would reject with FA_ERR_SHAPE.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * fa_bwd -- gradients of sum(O * dO) with respect to Q, K and V.
+ *
+ * Recomputes S and P block by block from Q, K and the saved LSE instead of
+ * reading a stored P ([Training-FA] §3 and §3.1; [Week-13] Step 2), using
+ * the closed form of the chain rule through softmax:
+ *   D_i = sum_k dO_ik O_ik,  dV = P^T dO,  dP = dO V^T,
+ *   dS = P * (dP - D 1^T),   dQ = scale * dS K,  dK = scale * dS^T Q.
+ * Three kernels run in order on `stream`: the D preprocess, a pass that is
+ * parallel over key blocks and accumulates dK and dV on chip, and a pass that
+ * is parallel over query blocks and accumulates dQ on chip (no atomics).
+ * Tiles dropped by causality or the block mask are skipped in both passes.
+ *
+ *   Q, K, V, O, dO  in : [B,H,N,d] dtype; O and LSE from fa_fwd with the
+ *                        same Q, K, V, scale, causal and block_mask
+ *   LSE             in : [B,H,N] fp32
+ *   dQ, dK, dV      out: [B,H,N,d] dtype (overwritten, not accumulated)
+ *   workspace       scratch of at least fa_bwd_workspace_bytes(B,H,N,d)
+ *                   bytes, 16-byte aligned, caller-owned; its contents are
+ *                   overwritten and need no initialisation.
+ */
+fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O,
+                 const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                 int B, int H, int N, int d, float scale, int causal,
+                 const unsigned char* block_mask, fa_dtype dtype,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The three phases of fa_bwd, callable one by one (fa_bwd is exactly
+ * fa_bwd_preprocess, then fa_bwd_dkdv, then fa_bwd_dq, on one stream).  The
+ * dK/dV and dQ passes only read what the preprocess wrote, so a caller may
+ * enqueue them on two streams that both wait for the preprocess.  Arguments
+ * have the meaning, layout and checks given for fa_bwd.
+ *
+ * fa_bwd_preprocess: workspace[i] = D_i = sum_k dO_ik O_ik (fp32), the
+ *   row term of dS = P * (dP - D 1^T).
+ * fa_bwd_dkdv: dK = scale * dS^T Q and dV = P^T dO, one work-group per 128
+ *   keys, recomputing S and P per query tile ([Training-FA] §3.1).
+ * fa_bwd_dq: dQ = scale * dS K, one work-group per 128 queries, recomputing
+ *   S, P and dP per key tile; no atomics.
+ */
+fa_status fa_bwd_preprocess(const void* O, const void* dO, int B, int H, int N, int d,
+                            fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                            void* stream);
+fa_status fa_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO,
+                      const float* LSE, void* dK, void* dV, int B, int H, int N, int d,
+                      float scale, int causal, const unsigned char* block_mask,
+                      fa_dtype dtype, const void* workspace, size_t workspace_bytes,
+                      void* stream);
+fa_status fa_bwd_dq(const void* Q, const void* K, const void* V, const void* dO,
+                    const float* LSE, void* dQ, int B, int H, int N, int d, float scale,
+                    int causal, const unsigned char* block_mask, fa_dtype dtype,
+                    const void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char* fa_status_str(fa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

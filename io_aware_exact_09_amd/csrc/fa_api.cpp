@@ -1,0 +1,221 @@
+// fa_api.cpp -- the C ABI declared in include/fa.h: argument validation
+// (pure host code that runs before anything is enqueued) and dispatch to the
+// kernel launchers.  Check order: NULL pointers, shape/dtype/scale,
+// alignment, workspace, overlaps.
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <initializer_list>
+
+#include "../../include/fa.h"
+#include "fa_launch.hpp"
+
+#define FA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+struct Buf {
+  const void* p;
+  uintptr_t bytes;
+  uintptr_t align;
+};
+
+bool overlaps(const Buf& a, const Buf& b) {
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+struct Shape {
+  int B, H, N, d;
+  fa_dtype dtype;
+  uintptr_t tensor_bytes() const { return (uintptr_t)B * H * N * d * (dtype == FA_BF16 ? 2 : 4); }
+  uintptr_t row_bytes() const { return (uintptr_t)B * H * N * 4; }
+  uintptr_t mask_bytes() const { const uintptr_t t = (N + 127) / 128; return t * t; }
+};
+
+fa_status check_shape(const Shape& s, float scale) {
+  if (s.dtype != FA_BF16 && s.dtype != FA_FP32) return FA_ERR_DTYPE;
+  if (s.B < 1 || s.H < 1 || s.N < 1) return FA_ERR_SHAPE;
+  if (s.d != 64 && s.d != 128) return FA_ERR_HEAD_DIM;
+  const long long bh = (long long)s.B * s.H;
+  const long long tiles = (s.N + 127LL) / 128;
+  if (bh > INT_MAX || (long long)s.N * s.d > INT_MAX || bh * tiles > INT_MAX ||
+      bh * s.N > INT_MAX)
+    return FA_ERR_SHAPE;
+  if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_ARG;
+  return FA_OK;
+}
+
+// ins/outs: every listed buffer must be non-NULL (callers list the optional
+// block mask only when present); the workspace is checked separately.
+fa_status check_buffers(std::initializer_list<Buf> ins, std::initializer_list<Buf> outs) {
+  for (const Buf& b : ins)
+    if (!b.p) return FA_ERR_NULL;
+  for (const Buf& b : outs)
+    if (!b.p) return FA_ERR_NULL;
+  return FA_OK;
+}
+
+fa_status check_layout(std::initializer_list<Buf> ins, std::initializer_list<Buf> outs,
+                       const Buf* ws, bool ws_is_output, size_t ws_need) {
+  for (const Buf& b : ins)
+    if ((uintptr_t)b.p % b.align) return FA_ERR_ALIGN;
+  for (const Buf& b : outs)
+    if ((uintptr_t)b.p % b.align) return FA_ERR_ALIGN;
+  if (ws && (!ws->p || ws->bytes < ws_need || (uintptr_t)ws->p % 16)) return FA_ERR_WORKSPACE;
+  for (const Buf& o : outs) {
+    for (const Buf& i : ins)
+      if (overlaps(o, i)) return FA_ERR_ALIAS;
+    for (const Buf& o2 : outs)
+      if (&o2 != &o && overlaps(o, o2)) return FA_ERR_ALIAS;
+    if (ws && overlaps(o, *ws)) return FA_ERR_ALIAS;
+  }
+  if (ws && ws_is_output)
+    for (const Buf& i : ins)
+      if (overlaps(*ws, i)) return FA_ERR_ALIAS;
+  return FA_OK;
+}
+
+fa::BwdArgs bwd_args(const Shape& s, float scale, int causal, const unsigned char* mask,
+                     void* stream) {
+  fa::BwdArgs a{};
+  a.mask = mask;
+  a.BH = s.B * s.H; a.N = s.N; a.d = s.d; a.T = (s.N + 127) / 128;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.bf16 = s.dtype == FA_BF16;
+  a.stream = static_cast<hipStream_t>(stream);
+  return a;
+}
+
+#define FA_TRY(expr)                 \
+  do {                               \
+    const fa_status st_ = (expr);    \
+    if (st_ != FA_OK) return st_;    \
+  } while (0)
+
+}  // namespace
+
+FA_EXPORT fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                           int B, int H, int N, int d, float scale, int causal,
+                           const unsigned char* block_mask, fa_dtype dtype, void* stream) {
+  FA_TRY(check_buffers({{Q, 0, 0}, {K, 0, 0}, {V, 0, 0}}, {{O, 0, 0}, {LSE, 0, 0}}));
+  const Shape s{B, H, N, d, dtype};
+  FA_TRY(check_shape(s, scale));
+  const uintptr_t tb = s.tensor_bytes(), lb = s.row_bytes();
+  const Buf q{Q, tb, 16}, k{K, tb, 16}, v{V, tb, 16}, o{O, tb, 16}, l{LSE, lb, 4};
+  const Buf m{block_mask, block_mask ? s.mask_bytes() : 0, 1};
+  FA_TRY(check_layout({q, k, v, m}, {o, l}, nullptr, false, 0));
+
+  fa::FwdArgs a{};
+  a.q = Q; a.k = K; a.v = V; a.o = O; a.lse = LSE;
+  a.mask = block_mask;
+  a.BH = B * H; a.N = N; a.d = d; a.T = (N + 127) / 128;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.bf16 = dtype == FA_BF16;
+  a.stream = static_cast<hipStream_t>(stream);
+  return fa::launch_fwd(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+FA_EXPORT size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
+  const Shape s{B, H, N, d, FA_BF16};
+  if (check_shape(s, 1.0f) != FA_OK) return 0;
+  return (size_t)s.row_bytes();
+}
+
+FA_EXPORT fa_status fa_bwd_preprocess(const void* O, const void* dO, int B, int H, int N, int d,
+                                      fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  FA_TRY(check_buffers({{O, 0, 0}, {dO, 0, 0}}, {}));
+  const Shape s{B, H, N, d, dtype};
+  FA_TRY(check_shape(s, 1.0f));
+  const uintptr_t tb = s.tensor_bytes();
+  const Buf ws{workspace, workspace_bytes, 16};
+  FA_TRY(check_layout({{O, tb, 16}, {dO, tb, 16}}, {}, &ws, true, s.row_bytes()));
+  fa::BwdArgs a = bwd_args(s, 1.0f, 0, nullptr, stream);
+  a.o = O; a.dout = dO; a.delta = static_cast<float*>(workspace);
+  return fa::launch_bwd_preprocess(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+FA_EXPORT fa_status fa_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO,
+                                const float* LSE, void* dK, void* dV, int B, int H, int N, int d,
+                                float scale, int causal, const unsigned char* block_mask,
+                                fa_dtype dtype, const void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  FA_TRY(check_buffers({{Q, 0, 0}, {K, 0, 0}, {V, 0, 0}, {dO, 0, 0}, {LSE, 0, 0}},
+                       {{dK, 0, 0}, {dV, 0, 0}}));
+  const Shape s{B, H, N, d, dtype};
+  FA_TRY(check_shape(s, scale));
+  const uintptr_t tb = s.tensor_bytes(), lb = s.row_bytes();
+  const Buf ws{workspace, workspace_bytes, 16};
+  const Buf m{block_mask, block_mask ? s.mask_bytes() : 0, 1};
+  FA_TRY(check_layout({{Q, tb, 16}, {K, tb, 16}, {V, tb, 16}, {dO, tb, 16}, {LSE, lb, 4}, m},
+                      {{dK, tb, 16}, {dV, tb, 16}}, &ws, false, lb));
+  fa::BwdArgs a = bwd_args(s, scale, causal, block_mask, stream);
+  a.q = Q; a.k = K; a.v = V; a.dout = dO; a.lse = LSE; a.dk = dK; a.dv = dV;
+  a.delta = static_cast<float*>(const_cast<void*>(workspace));
+  return fa::launch_bwd_dkdv(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+FA_EXPORT fa_status fa_bwd_dq(const void* Q, const void* K, const void* V, const void* dO,
+                              const float* LSE, void* dQ, int B, int H, int N, int d, float scale,
+                              int causal, const unsigned char* block_mask, fa_dtype dtype,
+                              const void* workspace, size_t workspace_bytes, void* stream) {
+  FA_TRY(check_buffers({{Q, 0, 0}, {K, 0, 0}, {V, 0, 0}, {dO, 0, 0}, {LSE, 0, 0}},
+                       {{dQ, 0, 0}}));
+  const Shape s{B, H, N, d, dtype};
+  FA_TRY(check_shape(s, scale));
+  const uintptr_t tb = s.tensor_bytes(), lb = s.row_bytes();
+  const Buf ws{workspace, workspace_bytes, 16};
+  const Buf m{block_mask, block_mask ? s.mask_bytes() : 0, 1};
+  FA_TRY(check_layout({{Q, tb, 16}, {K, tb, 16}, {V, tb, 16}, {dO, tb, 16}, {LSE, lb, 4}, m},
+                      {{dQ, tb, 16}}, &ws, false, lb));
+  fa::BwdArgs a = bwd_args(s, scale, causal, block_mask, stream);
+  a.q = Q; a.k = K; a.v = V; a.dout = dO; a.lse = LSE; a.dq = dQ;
+  a.delta = static_cast<float*>(const_cast<void*>(workspace));
+  return fa::launch_bwd_dq(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+FA_EXPORT fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O,
+                           const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                           int B, int H, int N, int d, float scale, int causal,
+                           const unsigned char* block_mask, fa_dtype dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  FA_TRY(check_buffers({{Q, 0, 0}, {K, 0, 0}, {V, 0, 0}, {O, 0, 0}, {dO, 0, 0}, {LSE, 0, 0}},
+                       {{dQ, 0, 0}, {dK, 0, 0}, {dV, 0, 0}}));
+  const Shape s{B, H, N, d, dtype};
+  FA_TRY(check_shape(s, scale));
+  const uintptr_t tb = s.tensor_bytes(), lb = s.row_bytes();
+  const Buf ws{workspace, workspace_bytes, 16};
+  const Buf m{block_mask, block_mask ? s.mask_bytes() : 0, 1};
+  FA_TRY(check_layout(
+      {{Q, tb, 16}, {K, tb, 16}, {V, tb, 16}, {O, tb, 16}, {dO, tb, 16}, {LSE, lb, 4}, m},
+      {{dQ, tb, 16}, {dK, tb, 16}, {dV, tb, 16}}, &ws, true, lb));
+
+  fa::BwdArgs a = bwd_args(s, scale, causal, block_mask, stream);
+  a.q = Q; a.k = K; a.v = V; a.o = O; a.dout = dO; a.lse = LSE;
+  a.dq = dQ; a.dk = dK; a.dv = dV;
+  a.delta = static_cast<float*>(workspace);
+  if (fa::launch_bwd_preprocess(a) != hipSuccess) return FA_ERR_LAUNCH;
+  if (fa::launch_bwd_dkdv(a) != hipSuccess) return FA_ERR_LAUNCH;
+  if (fa::launch_bwd_dq(a) != hipSuccess) return FA_ERR_LAUNCH;
+  return FA_OK;
+}
+
+FA_EXPORT const char* fa_status_str(fa_status s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "null pointer argument";
+    case FA_ERR_SHAPE: return "invalid shape (B, H, N must be >= 1 and sizes must fit int32)";
+    case FA_ERR_HEAD_DIM: return "head dimension must be 64 or 128";
+    case FA_ERR_DTYPE: return "unknown dtype";
+    case FA_ERR_ALIGN: return "misaligned tensor pointer (16 bytes; LSE 4 bytes)";
+    case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_ARG: return "scale must be finite and >= 0";
+    case FA_ERR_ALIAS: return "an output overlaps an input or another output";
+  }
+  return "unknown status";
+}

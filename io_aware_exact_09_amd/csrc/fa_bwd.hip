@@ -1,0 +1,459 @@
+// fa_bwd.hip -- exact-attention training backward for gfx950.
+//
+// The backward never reads a stored P: it recomputes S and P tile by tile
+// from Q, K and the per-row log-sum-exp saved by the forward, as the
+// recomputation scheme of the aivaro.ru answer on FlashAttention training
+// (§3 and §3.1) and the week-13 course page (snula.amonoc.com/course/ru/
+// week-13.html, Step 2) describe.  The gradients follow the chain rule
+// through softmax (the closed form that the page's garbled dQ/dK stand for):
+//
+//   D_i = sum_k dO_ik O_ik
+//   P_ij = 2^(S_ij * c - LSE_i * log2 e)      (c = scale * log2 e)
+//   dV_j = sum_i P_ij dO_i,   dP_ij = <dO_i, V_j>,   dS_ij = P_ij (dP_ij - D_i)
+//   dK_j = scale * sum_i dS_ij Q_i,   dQ_i = scale * sum_j dS_ij K_j
+//
+// Three kernels run in order on one stream:
+//   1. fa_bwd_delta: D = rowsum(dO * O) into the caller's workspace.
+//   2. fa_bwd_dkdv:  one work-group per 128 keys; walks the kept query tiles,
+//                    accumulates dK, dV on chip, writes them once.
+//   3. fa_bwd_dq:    one work-group per 128 queries; walks the kept key tiles,
+//                    accumulates dQ on chip, writes it once.
+// Splitting dQ into its own pass recomputes S and dP once more but needs no
+// atomics, so the result is deterministic.
+
+#include "fa_common.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+
+// ---------------------------------------------------------------------------
+// 1. D_i = sum_k dO_ik O_ik  (HBM-bound; one 16-byte chunk per lane)
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads)
+fa_bwd_delta_kernel(const T* __restrict__ O, const T* __restrict__ dO, float* __restrict__ delta,
+                    int rows) {
+  using E = Elem<T>;
+  constexpr int CH = E::kPerChunk;
+  constexpr int LPR = D / CH;                      // lanes per row
+  constexpr int RPB = kThreads / LPR;              // rows per block
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x * RPB + tid / LPR;
+  const int col = (tid % LPR) * CH;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(O + (size_t)row * D + col);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(dO + (size_t)row * D + col);
+    const T* pa = reinterpret_cast<const T*>(&a);
+    const T* pb = reinterpret_cast<const T*>(&b);
+#pragma unroll
+    for (int e = 0; e < CH; ++e) acc = fmaf(E::to_f32(pa[e]), E::to_f32(pb[e]), acc);
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && (tid % LPR) == 0) delta[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// 2. dK, dV: work-group = 128 keys (wave w: keys 32w..32w+31, lane l32 one
+//    key).  Per kept query tile of BQ = 64 rows:
+//      S   = Q_i K_j^T      (A = Q rows from LDS, B = K in registers)
+//      dP  = dO_i V_j^T     (A = dO rows from LDS, B = V in registers)
+//      P, dS elementwise in the C layout (query index per register)
+//      dV^T += dO_i^T P     (A = dO^T from LDS, B = P registers)
+//      dK^T += Q_i^T dS     (A = Q^T from LDS,  B = dS registers)
+// ---------------------------------------------------------------------------
+template <typename T>
+struct DkdvCfg {
+  static constexpr int BK = 128;                         // keys per work-group
+  static constexpr int BQ = sizeof(T) == 2 ? 64 : 32;   // query rows per tile
+  static constexpr int PAD = 16 / sizeof(T);
+};
+
+template <typename T, int D, bool CAUSAL, bool MASKED>
+__global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+                   const T* __restrict__ dO, const float* __restrict__ LSE,
+                   const float* __restrict__ delta, T* __restrict__ dK, T* __restrict__ dV,
+                   const uint8_t* __restrict__ mask, int BH, int N, int T_tiles, float c,
+                   float scale) {
+  using E = Elem<T>;
+  using frag = typename E::frag;
+  using Cfg = DkdvCfg<T>;
+  constexpr int BK = Cfg::BK, BQ = Cfg::BQ, PAD = Cfg::PAD;
+  constexpr int NQH = BQ / 32;            // 32-row query halves per tile
+  constexpr int NT = D / 16, ND = D / 32;
+  constexpr int LDR = D + PAD;            // row-major tiles
+  constexpr int LDT = BQ + PAD;           // transposed tiles
+  constexpr int CH = E::kPerChunk;
+  constexpr int TASKS = (BQ / 4) * (D / CH);
+  constexpr int TPT = (TASKS + kThreads - 1) / kThreads;
+
+  __shared__ __attribute__((aligned(16))) T sQ[BQ * LDR];
+  __shared__ __attribute__((aligned(16))) T sdO[BQ * LDR];
+  __shared__ __attribute__((aligned(16))) T sQt[D * LDT];
+  __shared__ __attribute__((aligned(16))) T sdOt[D * LDT];
+  __shared__ __attribute__((aligned(16))) float sL[BQ];   // LSE * log2e (+inf: no keys / pad)
+  __shared__ __attribute__((aligned(16))) float sD[BQ];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int nkb = (N + BK - 1) / BK;
+  const BlockCoord bc = map_block(blockIdx.x, nkb, BH, CAUSAL, false);
+  const int bh = bc.bh, kb = bc.blk, k0 = kb * BK;
+  const size_t head = (size_t)bh * N * D;
+  const T* Qh = Q + head;
+  const T* dOh = dO + head;
+  const float* Lh = LSE + (size_t)bh * N;
+  const float* Dh = delta + (size_t)bh * N;
+  const int kw = k0 + 32 * w;            // this wave's first key
+  const int krow = kw + l32;             // this lane's key
+
+  // K and V rows of this lane as B operands (natural d order).
+  frag kf[NT], vf[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    kf[t] = krow < N ? E::load(K + head + (size_t)krow * D + 16 * t + 8 * g) : E::zero();
+    vf[t] = krow < N ? E::load(V + head + (size_t)krow * D + 16 * t + 8 * g) : E::zero();
+  }
+
+  const int ntiles = (N + BQ - 1) / BQ;
+  const int first = CAUSAL ? k0 / BQ : 0;
+  const uint8_t* mcol = MASKED ? mask + kb : nullptr;     // mask[qi][kb], stride T
+  auto next_kept = [&](int i) {
+    if constexpr (MASKED) {
+      while (i < ntiles && mcol[(size_t)((i * BQ) / kMaskBlock) * T_tiles] == 0) ++i;
+    }
+    return i;
+  };
+
+  QuadTask<T, D> qt[TPT], ot[TPT];
+  float lpre = 0.f, dpre = 0.f;
+  auto load_tile = [&](int i) {
+    const int q0 = i * BQ;
+#pragma unroll
+    for (int x = 0; x < TPT; ++x) {
+      const int task = tid + x * kThreads;
+      if (task < TASKS) {
+        const int rq = task / (D / CH), col = (task % (D / CH)) * CH;
+        qt[x].load(Qh + (size_t)q0 * D, 4 * rq, col, N - q0);
+        ot[x].load(dOh + (size_t)q0 * D, 4 * rq, col, N - q0);
+      }
+    }
+    if (tid < BQ) {
+      const int q = q0 + tid;
+      const float l = q < N ? Lh[q] : neg_inf();
+      lpre = l == neg_inf() ? pos_inf() : l * kLog2e;
+      dpre = q < N ? Dh[q] : 0.f;
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int x = 0; x < TPT; ++x) {
+      const int task = tid + x * kThreads;
+      if (task < TASKS) {
+        const int rq = task / (D / CH), col = (task % (D / CH)) * CH;
+        qt[x].store_rows(sQ, LDR, 4 * rq, col);
+        qt[x].store_transposed(sQt, LDT, 4 * rq, col);
+        ot[x].store_rows(sdO, LDR, 4 * rq, col);
+        ot[x].store_transposed(sdOt, LDT, 4 * rq, col);
+      }
+    }
+    if (tid < BQ) { sL[tid] = lpre; sD[tid] = dpre; }
+  };
+
+  f32x16 dkacc[ND], dvacc[ND];
+#pragma unroll
+  for (int b = 0; b < ND; ++b) { dkacc[b] = f32x16{}; dvacc[b] = f32x16{}; }
+
+  int i = next_kept(first);
+  if (i < ntiles) load_tile(i);
+  while (i < ntiles) {
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    const int q0 = i * BQ;
+    const int in = next_kept(i + 1);
+    if (in < ntiles) load_tile(in);
+
+    const bool need_mask = CAUSAL && (q0 < kw + 31);
+#pragma unroll
+    for (int qh = 0; qh < NQH; ++qh) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const frag aq = E::load(sQ + (32 * qh + l32) * LDR + 16 * t + 8 * g);
+        s = E::mma(aq, kf[t], s);
+        const frag ao = E::load(sdO + (32 * qh + l32) * LDR + 16 * t + 8 * g);
+        dp = E::mma(ao, vf[t], dp);
+      }
+      // Register r holds query 32qh + 8(r/4) + 4g + r%4 of this tile.
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int qi = 32 * qh + 8 * a + 4 * g;
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(sL + qi);
+        const f32x4 dv = *reinterpret_cast<const f32x4*>(sD + qi);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int r = 4 * a + x;
+          float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[x]));
+          if (need_mask && krow > q0 + qi + x) p = 0.f;
+          s[r] = p;
+          dp[r] = p * (dp[r] - dv[x]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const frag pf = E::from_c(s, t);
+        const frag df = E::from_c(dp, t);
+        const int cc = 2 * qh + t;      // 16-row chunk of the query tile
+#pragma unroll
+        for (int b = 0; b < ND; ++b) {
+          const frag ao = E::load(sdOt + (32 * b + l32) * LDT + 16 * cc + 8 * g);
+          dvacc[b] = E::mma(ao, pf, dvacc[b]);
+          const frag aq = E::load(sQt + (32 * b + l32) * LDT + 16 * cc + 8 * g);
+          dkacc[b] = E::mma(aq, df, dkacc[b]);
+        }
+      }
+    }
+    i = in;
+  }
+
+  // dV^T / dK^T C layout: lane (key l32, g), register r -> d = 32b + 8(r/4) + 4g + r%4.
+  if (krow < N) {
+    T* dKr = dK + head + (size_t)krow * D;
+    T* dVr = dV + head + (size_t)krow * D;
+#pragma unroll
+    for (int b = 0; b < ND; ++b)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int d0 = 32 * b + 8 * a + 4 * g;
+        E::store4(dVr + d0, dvacc[b][4 * a], dvacc[b][4 * a + 1], dvacc[b][4 * a + 2],
+                  dvacc[b][4 * a + 3]);
+        E::store4(dKr + d0, dkacc[b][4 * a] * scale, dkacc[b][4 * a + 1] * scale,
+                  dkacc[b][4 * a + 2] * scale, dkacc[b][4 * a + 3] * scale);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. dQ: work-group = 128 queries (wave w: rows 32w..32w+31, lane pair one
+//    row), same walk over key tiles as the forward:
+//      S^T  = K_j Q_i^T     (A = K rows from LDS, B = Q registers)
+//      dP^T = V_j dO_i^T    (A = V rows from LDS, B = dO registers)
+//      P^T, dS^T elementwise with this lane's own LSE_i and D_i
+//      dQ^T += K_j^T dS^T   (A = K^T from LDS, B = dS^T registers)
+// ---------------------------------------------------------------------------
+template <typename T>
+struct DqCfg {
+  static constexpr int BR = 128;
+  static constexpr int BC = sizeof(T) == 2 ? 64 : 32;
+  static constexpr int PAD = 16 / sizeof(T);
+};
+
+template <typename T, int D, bool CAUSAL, bool MASKED>
+__global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+                 const T* __restrict__ dO, const float* __restrict__ LSE,
+                 const float* __restrict__ delta, T* __restrict__ dQ,
+                 const uint8_t* __restrict__ mask, int BH, int N, int T_tiles, float c,
+                 float scale) {
+  using E = Elem<T>;
+  using frag = typename E::frag;
+  using Cfg = DqCfg<T>;
+  constexpr int BR = Cfg::BR, BC = Cfg::BC, PAD = Cfg::PAD;
+  constexpr int NH = BC / 32, NT = D / 16, ND = D / 32;
+  constexpr int LDR = D + PAD, LDT = BC + PAD;
+  constexpr int CH = E::kPerChunk;
+  constexpr int TASKS = (BC / 4) * (D / CH);
+  constexpr int TPT = (TASKS + kThreads - 1) / kThreads;
+
+  __shared__ __attribute__((aligned(16))) T sK[BC * LDR];
+  __shared__ __attribute__((aligned(16))) T sV[BC * LDR];
+  __shared__ __attribute__((aligned(16))) T sKt[D * LDT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int nqb = (N + BR - 1) / BR;
+  const BlockCoord bc = map_block(blockIdx.x, nqb, BH, CAUSAL, true);
+  const int bh = bc.bh, q0 = bc.blk * BR;
+  const size_t head = (size_t)bh * N * D;
+  const T* Kh = K + head;
+  const T* Vh = V + head;
+  const int qrow = q0 + 32 * w + l32;
+
+  frag qf[NT], of[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    qf[t] = qrow < N ? E::load(Q + head + (size_t)qrow * D + 16 * t + 8 * g) : E::zero();
+    of[t] = qrow < N ? E::load(dO + head + (size_t)qrow * D + 16 * t + 8 * g) : E::zero();
+  }
+  float lse2 = pos_inf(), dval = 0.f;
+  if (qrow < N) {
+    const float l = LSE[(size_t)bh * N + qrow];
+    lse2 = l == neg_inf() ? pos_inf() : l * kLog2e;
+    dval = delta[(size_t)bh * N + qrow];
+  }
+
+  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+  const int ntiles = (kv_end + BC - 1) / BC;
+  const uint8_t* mrow = MASKED ? mask + (size_t)(q0 / kMaskBlock) * T_tiles : nullptr;
+  auto next_kept = [&](int j) {
+    if constexpr (MASKED) {
+      while (j < ntiles && mrow[(j * BC) / kMaskBlock] == 0) ++j;
+    }
+    return j;
+  };
+
+  QuadTask<T, D> kt[TPT], vt[TPT];
+  auto load_tile = [&](int j) {
+    const int kv0 = j * BC;
+#pragma unroll
+    for (int x = 0; x < TPT; ++x) {
+      const int task = tid + x * kThreads;
+      if (task < TASKS) {
+        const int rq = task / (D / CH), col = (task % (D / CH)) * CH;
+        kt[x].load(Kh + (size_t)kv0 * D, 4 * rq, col, N - kv0);
+        vt[x].load(Vh + (size_t)kv0 * D, 4 * rq, col, N - kv0);
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int x = 0; x < TPT; ++x) {
+      const int task = tid + x * kThreads;
+      if (task < TASKS) {
+        const int rq = task / (D / CH), col = (task % (D / CH)) * CH;
+        kt[x].store_rows(sK, LDR, 4 * rq, col);
+        kt[x].store_transposed(sKt, LDT, 4 * rq, col);
+        vt[x].store_rows(sV, LDR, 4 * rq, col);
+      }
+    }
+  };
+
+  f32x16 dqacc[ND];
+#pragma unroll
+  for (int b = 0; b < ND; ++b) dqacc[b] = f32x16{};
+
+  int j = next_kept(0);
+  if (j < ntiles) load_tile(j);
+  while (j < ntiles) {
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    const int kv0 = j * BC;
+    const int jn = next_kept(j + 1);
+    if (jn < ntiles) load_tile(jn);
+
+    const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > q0 + 32 * w);
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const frag ak = E::load(sK + (32 * h + l32) * LDR + 16 * t + 8 * g);
+        s = E::mma(ak, qf[t], s);
+        const frag av = E::load(sV + (32 * h + l32) * LDR + 16 * t + 8 * g);
+        dp = E::mma(av, of[t], dp);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
+        if (need_mask) {
+          const int kv = kv0 + 32 * h + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (kv >= N || (CAUSAL && kv > qrow)) p = 0.f;
+        }
+        dp[r] = p * (dp[r] - dval);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const frag df = E::from_c(dp, t);
+        const int cc = 2 * h + t;
+#pragma unroll
+        for (int b = 0; b < ND; ++b) {
+          const frag a = E::load(sKt + (32 * b + l32) * LDT + 16 * cc + 8 * g);
+          dqacc[b] = E::mma(a, df, dqacc[b]);
+        }
+      }
+    }
+    j = jn;
+  }
+
+  if (qrow < N) {
+    T* dQr = dQ + head + (size_t)qrow * D;
+#pragma unroll
+    for (int b = 0; b < ND; ++b)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        E::store4(dQr + 32 * b + 8 * a + 4 * g, dqacc[b][4 * a] * scale,
+                  dqacc[b][4 * a + 1] * scale, dqacc[b][4 * a + 2] * scale,
+                  dqacc[b][4 * a + 3] * scale);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launch
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+static hipError_t launch_pre_t(const BwdArgs& a) {
+  constexpr int RPB = kThreads / (D / Elem<T>::kPerChunk);
+  const int rows = a.BH * a.N;
+  hipLaunchKernelGGL((fa_bwd_delta_kernel<T, D>), dim3((rows + RPB - 1) / RPB), dim3(kThreads),
+                     0, a.stream, static_cast<const T*>(a.o), static_cast<const T*>(a.dout),
+                     a.delta, rows);
+  return hipGetLastError();
+}
+
+template <typename T, int D, bool CAUSAL, bool MASKED>
+static hipError_t launch_dkdv_t(const BwdArgs& a) {
+  const int nkb = (a.N + DkdvCfg<T>::BK - 1) / DkdvCfg<T>::BK;
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, CAUSAL, MASKED>), dim3(nkb * a.BH),
+                     dim3(kThreads), 0, a.stream, static_cast<const T*>(a.q),
+                     static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                     static_cast<const T*>(a.dout), a.lse, a.delta, static_cast<T*>(a.dk),
+                     static_cast<T*>(a.dv), a.mask, a.BH, a.N, a.T, a.scale * kLog2e, a.scale);
+  return hipGetLastError();
+}
+
+template <typename T, int D, bool CAUSAL, bool MASKED>
+static hipError_t launch_dq_t(const BwdArgs& a) {
+  const int nqb = (a.N + DqCfg<T>::BR - 1) / DqCfg<T>::BR;
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, CAUSAL, MASKED>), dim3(nqb * a.BH), dim3(kThreads),
+                     0, a.stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                     static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
+                     static_cast<T*>(a.dq), a.mask, a.BH, a.N, a.T, a.scale * kLog2e, a.scale);
+  return hipGetLastError();
+}
+
+// Dispatch on (dtype, d, causal, masked) to a kernel instance.
+#define FA_DISPATCH(LAUNCH, a)                                                       \
+  do {                                                                               \
+    const bool cz = (a).causal, mk = (a).mask != nullptr;                            \
+    if ((a).bf16) {                                                                  \
+      if ((a).d == 64) {                                                             \
+        if (cz) return mk ? LAUNCH<__bf16, 64, true, true>(a) : LAUNCH<__bf16, 64, true, false>(a); \
+        return mk ? LAUNCH<__bf16, 64, false, true>(a) : LAUNCH<__bf16, 64, false, false>(a);       \
+      }                                                                              \
+      if (cz) return mk ? LAUNCH<__bf16, 128, true, true>(a) : LAUNCH<__bf16, 128, true, false>(a); \
+      return mk ? LAUNCH<__bf16, 128, false, true>(a) : LAUNCH<__bf16, 128, false, false>(a);       \
+    }                                                                                \
+    if ((a).d == 64) {                                                               \
+      if (cz) return mk ? LAUNCH<float, 64, true, true>(a) : LAUNCH<float, 64, true, false>(a);     \
+      return mk ? LAUNCH<float, 64, false, true>(a) : LAUNCH<float, 64, false, false>(a);           \
+    }                                                                                \
+    if (cz) return mk ? LAUNCH<float, 128, true, true>(a) : LAUNCH<float, 128, true, false>(a);     \
+    return mk ? LAUNCH<float, 128, false, true>(a) : LAUNCH<float, 128, false, false>(a);           \
+  } while (0)
+
+hipError_t launch_bwd_preprocess(const BwdArgs& a) {
+  if (a.bf16) return a.d == 64 ? launch_pre_t<__bf16, 64>(a) : launch_pre_t<__bf16, 128>(a);
+  return a.d == 64 ? launch_pre_t<float, 64>(a) : launch_pre_t<float, 128>(a);
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a) { FA_DISPATCH(launch_dkdv_t, a); }
+
+hipError_t launch_bwd_dq(const BwdArgs& a) { FA_DISPATCH(launch_dq_t, a); }
+
+}  // namespace fa

@@ -1,0 +1,257 @@
+// fa_fwd.hip -- tiled exact-attention forward for gfx950.
+//
+// One work-group (4 waves) owns 128 query rows of one (batch, head); wave w
+// owns rows 32w..32w+31 and each lane-pair (l32, l32+32) owns one query row.
+// The work-group walks the kept key/value tiles of BC keys:
+//
+//   S^T = K_j Q_i^T      (MFMA; K from LDS, Q held in registers)
+//   mask causal / tail / nothing, running max m, P~ = 2^(S*c - m),
+//   rescale l and O by 2^(m_old - m_new) when the max moved,
+//   O^T += V_j^T P~^T    (MFMA; V stored transposed in LDS, P~ from registers)
+//
+// and writes O = O_acc / l and LSE = (m + log2 l) ln 2 at the end.  This is
+// the per-block update of the FlashAttention reading guide (xyznot.com/tr/
+// paper/2205.14135, "Yöntem" steps 1-4, with the two-part rule of "Artımsal
+// Softmax Takibi") in its deferred-normalisation form (snula.amonoc.com/
+// course/ru/week-13.html, Step 2: keep (m, d, o) per query block, scale the
+// old d and o by e^(m_old - m_new) on a new maximum).  Scores live in the
+// log2 domain: c = scale * log2(e), so every exponential is one v_exp_f32.
+// A row whose running max is still -inf uses 0 as the subtrahend, so no
+// 2^(-inf - (-inf)) is formed (week-13 page, "Типичные ошибки").
+//
+// Computing S^T (keys as the MFMA rows) puts one query row in each lane:
+// the row max needs one cross-lane exchange (lane l with l^32), the row sum
+// stays per lane until the end, and the C registers of S^T are already the B
+// operand of the P V product (C-shaped contraction order, see fa_common.hpp).
+
+#include "fa_common.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+
+template <typename T>
+struct FwdCfg {
+  static constexpr int BR = 128;                          // query rows per work-group
+  static constexpr int BC = sizeof(T) == 2 ? 64 : 32;     // keys per tile
+  static constexpr int PAD = 16 / sizeof(T);              // 16-byte row padding
+};
+
+template <typename T, int D, bool CAUSAL, bool MASKED>
+__global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+              T* __restrict__ O, float* __restrict__ LSE, const uint8_t* __restrict__ mask,
+              int BH, int N, int T_tiles, float c /* scale*log2e */) {
+  using E = Elem<T>;
+  using frag = typename E::frag;
+  using Cfg = FwdCfg<T>;
+  constexpr int BR = Cfg::BR, BC = Cfg::BC, PAD = Cfg::PAD;
+  constexpr int NH = BC / 32;              // 32-key halves per tile
+  constexpr int NT = D / 16;               // 16-wide d chunks
+  constexpr int ND = D / 32;               // 32-wide d blocks of O^T
+  constexpr int LDK = D + PAD;             // sK row stride (elements)
+  constexpr int LDV = BC + PAD;            // sVt row stride
+  constexpr int CH = E::kPerChunk;         // elements per 16-byte chunk
+  constexpr int KTASKS = (BC / 4) * (D / CH);
+  constexpr int VTASKS = KTASKS;
+  constexpr int KPT = (KTASKS + kThreads - 1) / kThreads;   // tasks per thread
+  constexpr int VPT = (VTASKS + kThreads - 1) / kThreads;
+
+  __shared__ __attribute__((aligned(16))) T sK[BC * LDK];
+  __shared__ __attribute__((aligned(16))) T sVt[D * LDV];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int nqb = (N + BR - 1) / BR;
+  const BlockCoord bc = map_block(blockIdx.x, nqb, BH, CAUSAL, true);
+  const int bh = bc.bh, q0 = bc.blk * BR;
+  const size_t head = (size_t)bh * N * D;
+  const T* Qh = Q + head;
+  const T* Kh = K + head;
+  const T* Vh = V + head;
+  const int qrow = q0 + 32 * w + l32;
+
+  // Query fragments (B operand, natural order): Q[qrow][16t + 8g .. +7].
+  frag qf[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    qf[t] = qrow < N ? E::load(Qh + (size_t)qrow * D + 16 * t + 8 * g) : E::zero();
+
+  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+  const int ntiles = (kv_end + BC - 1) / BC;
+  const uint8_t* mrow = MASKED ? mask + (size_t)(q0 / kMaskBlock) * T_tiles : nullptr;
+  auto next_kept = [&](int j) {
+    if constexpr (MASKED) {
+      while (j < ntiles && mrow[(j * BC) / kMaskBlock] == 0) ++j;
+    }
+    return j;
+  };
+
+  QuadTask<T, D> kt[KPT], vt[VPT];
+  auto load_tile = [&](int j) {
+    const int kv0 = j * BC;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int task = tid + i * kThreads;
+      if (task < KTASKS) {
+        const int rq = task / (D / CH), col = (task % (D / CH)) * CH;
+        kt[i].load(Kh + (size_t)kv0 * D, 4 * rq, col, N - kv0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int task = tid + i * kThreads;
+      if (task < VTASKS) {
+        const int rq = task / (D / CH), col = (task % (D / CH)) * CH;
+        vt[i].load(Vh + (size_t)kv0 * D, 4 * rq, col, N - kv0);
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int task = tid + i * kThreads;
+      if (task < KTASKS) {
+        const int rq = task / (D / CH), col = (task % (D / CH)) * CH;
+        kt[i].store_rows(sK, LDK, 4 * rq, col);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int task = tid + i * kThreads;
+      if (task < VTASKS) {
+        const int rq = task / (D / CH), col = (task % (D / CH)) * CH;
+        vt[i].store_transposed(sVt, LDV, 4 * rq, col);
+      }
+    }
+  };
+
+  f32x16 oacc[ND];
+#pragma unroll
+  for (int b = 0; b < ND; ++b) oacc[b] = f32x16{};
+  float m_run = neg_inf();   // running max of S*c (log2 domain), same in both lane halves
+  float l_run = 0.f;         // this lane's partial row sum
+
+  int j = next_kept(0);
+  if (j < ntiles) load_tile(j);
+  while (j < ntiles) {
+    __syncthreads();                 // everyone is done reading the previous tile
+    store_tile();
+    __syncthreads();
+    const int kv0 = j * BC;
+    const int jn = next_kept(j + 1);
+    if (jn < ntiles) load_tile(jn);  // in flight while this tile is computed
+
+    // ---- S^T = K_j Q^T -------------------------------------------------
+    f32x16 s[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      s[h] = f32x16{};
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const frag a = E::load(sK + (32 * h + l32) * LDK + 16 * t + 8 * g);
+        s[h] = E::mma(a, qf[t], s[h]);
+      }
+    }
+
+    // ---- mask (diagonal / tail tiles only) -------------------------------
+    const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > q0 + 32 * w);
+    uint32_t keep_bits = 0xffffffffu;
+    if (need_mask) {
+      keep_bits = 0;
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kv = kv0 + 32 * h + 8 * (r >> 2) + 4 * g + (r & 3);
+          const bool keep = kv < N && (!CAUSAL || kv <= qrow);
+          keep_bits |= (keep ? 1u : 0u) << (16 * h + r);
+          if (!keep) s[h][r] = neg_inf();
+        }
+    }
+
+    // ---- online softmax ----------------------------------------------------
+    float mx = neg_inf();
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[h][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_tile = mx == neg_inf() ? neg_inf() : mx * c;
+    const float m_new = fmaxf(m_run, m_tile);
+    const float m_use = m_new == neg_inf() ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);   // 0 while m_run = -inf
+    float psum = 0.f;
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = __builtin_amdgcn_exp2f(fmaf(s[h][r], c, -m_use));
+        if (need_mask && !((keep_bits >> (16 * h + r)) & 1u)) p = 0.f;
+        s[h][r] = p;
+        psum += p;
+      }
+    l_run = fmaf(l_run, alpha, psum);
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int b = 0; b < ND; ++b) oacc[b] *= alpha;
+    }
+    m_run = m_new;
+
+    // ---- O^T += V_j^T P^T ----------------------------------------------------
+    frag pf[NH][2];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      pf[h][0] = E::from_c(s[h], 0);
+      pf[h][1] = E::from_c(s[h], 1);
+    }
+#pragma unroll
+    for (int b = 0; b < ND; ++b)
+#pragma unroll
+      for (int cc = 0; cc < 2 * NH; ++cc) {
+        const frag a = E::load(sVt + (32 * b + l32) * LDV + 16 * cc + 8 * g);
+        oacc[b] = E::mma(a, pf[cc >> 1][cc & 1], oacc[b]);
+      }
+    j = jn;
+  }
+
+  // ---- epilogue ----------------------------------------------------------------
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  if (qrow < N) {
+    T* Orow = O + head + (size_t)qrow * D;
+#pragma unroll
+    for (int b = 0; b < ND; ++b)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        E::store4(Orow + 32 * b + 8 * a + 4 * g, oacc[b][4 * a] * inv, oacc[b][4 * a + 1] * inv,
+                  oacc[b][4 * a + 2] * inv, oacc[b][4 * a + 3] * inv);
+    if (g == 0)
+      LSE[(size_t)bh * N + qrow] =
+          l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : neg_inf();
+  }
+}
+
+template <typename T, int D, bool CAUSAL, bool MASKED>
+static hipError_t launch_fwd_t(const FwdArgs& a) {
+  const int nqb = (a.N + FwdCfg<T>::BR - 1) / FwdCfg<T>::BR;
+  const dim3 grid(nqb * a.BH), block(kThreads);
+  hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, MASKED>), grid, block, 0, a.stream,
+                     static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                     static_cast<const T*>(a.v), static_cast<T*>(a.o), a.lse, a.mask, a.BH,
+                     a.N, a.T, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_fwd_d(const FwdArgs& a) {
+  if (a.causal) return a.mask ? launch_fwd_t<T, D, true, true>(a) : launch_fwd_t<T, D, true, false>(a);
+  return a.mask ? launch_fwd_t<T, D, false, true>(a) : launch_fwd_t<T, D, false, false>(a);
+}
+
+hipError_t launch_fwd(const FwdArgs& a) {
+  if (a.bf16) return a.d == 64 ? launch_fwd_d<__bf16, 64>(a) : launch_fwd_d<__bf16, 128>(a);
+  return a.d == 64 ? launch_fwd_d<float, 64>(a) : launch_fwd_d<float, 128>(a);
+}
+
+}  // namespace fa

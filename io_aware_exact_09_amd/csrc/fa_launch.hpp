@@ -1,0 +1,37 @@
+// fa_launch.hpp -- internal launch interface between the C-ABI layer and the
+// kernels.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q; const void* k; const void* v;
+  void* o; float* lse;
+  const uint8_t* mask;     // nullptr = dense
+  int BH, N, d, T;         // T = ceil(N / 128) (mask side)
+  float scale;
+  bool causal, bf16;
+  hipStream_t stream;
+};
+
+struct BwdArgs {
+  const void* q; const void* k; const void* v; const void* o; const void* dout;
+  const float* lse;
+  void* dq; void* dk; void* dv;
+  float* delta;            // workspace: D_i = rowsum(dO * O), [BH * N] fp32
+  const uint8_t* mask;
+  int BH, N, d, T;
+  float scale;
+  bool causal, bf16;
+  hipStream_t stream;
+};
+
+hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_bwd_preprocess(const BwdArgs& a);
+hipError_t launch_bwd_dkdv(const BwdArgs& a);
+hipError_t launch_bwd_dq(const BwdArgs& a);
+
+}  // namespace fa

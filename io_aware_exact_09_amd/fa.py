@@ -1,0 +1,228 @@
+"""Python binding of libfa.so (the C ABI in include/fa.h).
+
+Argument marshalling only: the functions below check that the torch tensors
+have the layout the C ABI documents, pass raw device pointers and the
+caller's current HIP stream to ``fa_fwd`` / ``fa_bwd``, and raise
+``FAError`` on a non-OK status.  Every step of the computation runs in the
+HIP kernels; there is no fallback.  If libfa.so is missing or cannot be
+loaded, the first call raises.
+
+torch is imported before the library is loaded so that libfa.so binds to the
+HIP runtime torch has already mapped (both carry the soname libamdhip64.so.7).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fa.h")
+
+FA_BF16, FA_FP32 = 0, 1
+MASK_BLOCK = 128
+
+STATUS = {
+    0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEAD_DIM",
+    4: "FA_ERR_DTYPE", 5: "FA_ERR_ALIGN", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_LAUNCH",
+    8: "FA_ERR_ARG", 9: "FA_ERR_ALIAS",
+}
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str, msg: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa.so (once) and declare its C signatures."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"libfa.so not found at {path}; build it first "
+                "(python -m io_aware_exact_09_amd.build)")
+        lib = ctypes.CDLL(path, mode=ctypes.RTLD_GLOBAL)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp]
+        lib.fa_fwd.restype = i
+        lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
+        lib.fa_bwd_workspace_bytes.restype = sz
+        lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i,
+                               vp, sz, vp]
+        lib.fa_bwd.restype = i
+        lib.fa_bwd_preprocess.argtypes = [vp, vp, i, i, i, i, i, vp, sz, vp]
+        lib.fa_bwd_preprocess.restype = i
+        lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz,
+                                    vp]
+        lib.fa_bwd_dkdv.restype = i
+        lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp]
+        lib.fa_bwd_dq.restype = i
+        lib.fa_status_str.argtypes = [i]
+        lib.fa_status_str.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def header_functions(path: str = HEADER_PATH) -> list[str]:
+    """Names of the functions include/fa.h declares."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"\b(fa_[a-z_]+)\s*\(", text)
+
+
+def status_str(status: int) -> str:
+    return load_library().fa_status_str(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise FAError(status, where, status_str(status))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_FP32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_tensors(ref: torch.Tensor, named: dict):
+    if ref.dim() != 4:
+        raise ValueError("tensors must be [B, H, N, d]")
+    for name, t in named.items():
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def fa_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(load_library().fa_bwd_workspace_bytes(B, H, N, d))
+
+
+def fa_fwd(q, k, v, o, lse, scale: float, causal: bool = False, block_mask=None,
+           stream=None) -> None:
+    """Enqueue the forward on ``stream`` (default: torch's current stream).
+
+    q, k, v, o: [B,H,N,d] bf16 or fp32 device tensors; lse: [B,H,N] fp32;
+    block_mask: None or a uint8 [ceil(N/128)]^2 device tensor.
+    """
+    lib = load_library()
+    _check_tensors(q, dict(q=q, k=k, v=v, o=o, lse=lse))
+    B, H, N, d = q.shape
+    if block_mask is not None:
+        _check_tensors(q, dict(block_mask=block_mask))
+        if block_mask.dtype != torch.uint8:
+            raise TypeError("block_mask must be uint8")
+    st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                    int(bool(causal)), _ptr(block_mask), _dtype_code(q), _stream(stream))
+    _check(st, "fa_fwd")
+
+
+def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = False,
+           block_mask=None, workspace=None, stream=None) -> None:
+    """Enqueue the backward.  ``workspace``: a device tensor of at least
+    fa_bwd_workspace_bytes(B, H, N, d) bytes (allocated here if None)."""
+    lib = load_library()
+    _check_tensors(q, dict(q=q, k=k, v=v, o=o, do=do, lse=lse, dq=dq, dk=dk, dv=dv))
+    B, H, N, d = q.shape
+    need = fa_bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    if block_mask is not None:
+        _check_tensors(q, dict(block_mask=block_mask))
+        if block_mask.dtype != torch.uint8:
+            raise TypeError("block_mask must be uint8")
+    st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                    _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
+                    _ptr(block_mask), _dtype_code(q), _ptr(workspace), wbytes,
+                    _stream(stream))
+    _check(st, "fa_bwd")
+
+
+def _mask_ok(q, block_mask):
+    if block_mask is not None:
+        _check_tensors(q, dict(block_mask=block_mask))
+        if block_mask.dtype != torch.uint8:
+            raise TypeError("block_mask must be uint8")
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def fa_bwd_preprocess(o, do, workspace, stream=None) -> None:
+    """D_i = rowsum(dO * O) into ``workspace`` (first phase of fa_bwd)."""
+    lib = load_library()
+    _check_tensors(o, dict(o=o, do=do, workspace=workspace))
+    B, H, N, d = o.shape
+    st = lib.fa_bwd_preprocess(_ptr(o), _ptr(do), B, H, N, d, _dtype_code(o), _ptr(workspace),
+                               _nbytes(workspace), _stream(stream))
+    _check(st, "fa_bwd_preprocess")
+
+
+def fa_bwd_dkdv(q, k, v, do, lse, dk, dv, scale, causal=False, block_mask=None,
+                workspace=None, stream=None) -> None:
+    """dK, dV pass (second phase of fa_bwd); ``workspace`` holds D."""
+    lib = load_library()
+    _check_tensors(q, dict(q=q, k=k, v=v, do=do, lse=lse, dk=dk, dv=dv, workspace=workspace))
+    _mask_ok(q, block_mask)
+    B, H, N, d = q.shape
+    st = lib.fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dk), _ptr(dv),
+                         B, H, N, d, float(scale), int(bool(causal)), _ptr(block_mask),
+                         _dtype_code(q), _ptr(workspace), _nbytes(workspace), _stream(stream))
+    _check(st, "fa_bwd_dkdv")
+
+
+def fa_bwd_dq(q, k, v, do, lse, dq, scale, causal=False, block_mask=None, workspace=None,
+              stream=None) -> None:
+    """dQ pass (third phase of fa_bwd); ``workspace`` holds D."""
+    lib = load_library()
+    _check_tensors(q, dict(q=q, k=k, v=v, do=do, lse=lse, dq=dq, workspace=workspace))
+    _mask_ok(q, block_mask)
+    B, H, N, d = q.shape
+    st = lib.fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dq), B, H, N, d,
+                       float(scale), int(bool(causal)), _ptr(block_mask), _dtype_code(q),
+                       _ptr(workspace), _nbytes(workspace), _stream(stream))
+    _check(st, "fa_bwd_dq")
+
+
+# Convenience wrappers that allocate outputs with torch (memory plumbing only).
+
+def forward(q, k, v, scale: float, causal: bool = False, block_mask=None, stream=None):
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, scale, causal, block_mask, stream)
+    return o, lse
+
+
+def backward(q, k, v, o, do, lse, scale: float, causal: bool = False, block_mask=None,
+             workspace=None, stream=None):
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale, causal, block_mask, workspace, stream)
+    return dq, dk, dv

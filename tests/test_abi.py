@@ -1,0 +1,137 @@
+"""The C-ABI library loads, exports what include/fa.h declares, and rejects
+invalid arguments before launching anything.
+
+These tests make no compute call: every fa_fwd/fa_bwd call below carries at
+least one invalid argument, and validation is pure host code that returns
+before the HIP runtime is touched.  Pointers are fake, never dereferenced.
+"""
+
+import ctypes
+import subprocess
+
+import pytest
+
+from io_aware_exact_09_amd import fa
+
+BF16, FP32 = fa.FA_BF16, fa.FA_FP32
+A = 0x7f0000000000            # fake, 16-byte aligned, never dereferenced
+MB = 1 << 24                   # spacing between fake tensors
+
+
+def p(i, off=0):
+    return ctypes.c_void_p(A + i * MB + off)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fa.load_library()
+
+
+def test_header_symbols_are_exported(lib):
+    names = fa.header_functions()
+    assert set(names) == {"fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
+                          "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq"}
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for n in names:
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+    # Nothing else leaks out of the library's C ABI namespace.
+    assert {e for e in exported if e.startswith("fa_")} == set(names)
+
+
+def test_status_strings(lib):
+    for code, name in fa.STATUS.items():
+        s = fa.status_str(code)
+        assert s and s != "unknown status", name
+    assert fa.status_str(42) == "unknown status"
+
+
+def test_workspace_bytes(lib):
+    assert fa.fa_bwd_workspace_bytes(2, 16, 4096, 128) == 4 * 2 * 16 * 4096
+    assert fa.fa_bwd_workspace_bytes(1, 8, 16384, 128) == 4 * 8 * 16384
+    assert fa.fa_bwd_workspace_bytes(1, 1, 1, 64) == 4
+    assert fa.fa_bwd_workspace_bytes(0, 1, 1, 64) == 0
+    assert fa.fa_bwd_workspace_bytes(1, 1, 1, 96) == 0
+    assert fa.fa_bwd_workspace_bytes(1, 1, 1 << 30, 128) == 0     # N*d overflows int32
+
+
+def fwd(lib, q=p(0), k=p(1), v=p(2), o=p(3), lse=p(4), B=1, H=2, N=128, d=64, scale=0.125,
+        causal=0, mask=None, dtype=BF16):
+    return lib.fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, mask, dtype, None)
+
+
+def bwd(lib, q=p(0), k=p(1), v=p(2), o=p(3), do=p(4), lse=p(5), dq=p(6), dk=p(7), dv=p(8),
+        B=1, H=2, N=128, d=64, scale=0.125, causal=0, mask=None, dtype=BF16, ws=p(9),
+        wsb=1 << 20):
+    return lib.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, B, H, N, d, scale, causal, mask, dtype,
+                      ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(lse=None), 1), (dict(o=None), 1),
+    (dict(B=0), 2), (dict(H=-1), 2), (dict(N=0), 2), (dict(N=1 << 30, d=128), 2),
+    (dict(d=96), 3), (dict(d=32), 3), (dict(d=256), 3),
+    (dict(dtype=7), 4),
+    (dict(q=p(0, 8)), 5), (dict(o=p(3, 4)), 5), (dict(lse=p(4, 2)), 5),
+    (dict(scale=float("nan")), 8), (dict(scale=float("inf")), 8), (dict(scale=-0.5), 8),
+    (dict(o=p(0, 64)), 9), (dict(lse=p(2, 16)), 9), (dict(o=p(4)), 9),
+    (dict(mask=p(3, 32)), 9),
+])
+def test_fwd_validation(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(do=None), 1), (dict(dv=None), 1), (dict(lse=None), 1),
+    (dict(N=0), 2), (dict(d=80), 3), (dict(dtype=-1), 4),
+    (dict(dk=p(7, 8)), 5), (dict(lse=p(5, 1)), 5),
+    (dict(ws=None), 6), (dict(wsb=4 * 2 * 128 - 1), 6), (dict(ws=p(9, 4)), 6),
+    (dict(scale=-1.0), 8),
+    (dict(dq=p(0, 16)), 9), (dict(dk=p(6, 16)), 9), (dict(ws=p(5)), 9), (dict(dv=p(9)), 9),
+    (dict(mask=p(8, 16)), 9),
+])
+def test_bwd_validation(lib, kw, code):
+    assert bwd(lib, **kw) == code
+
+
+def test_status_codes_match_header():
+    text = open(fa.HEADER_PATH).read()
+    for code, name in fa.STATUS.items():
+        assert f"{name} = {code}" in text, name
+
+
+def test_phase_validation(lib):
+    # preprocess: (O, dO, B, H, N, d, dtype, ws, wsb, stream)
+    assert lib.fa_bwd_preprocess(None, p(1), 1, 2, 128, 64, BF16, p(2), 1 << 20, None) == 1
+    assert lib.fa_bwd_preprocess(p(0), p(1), 1, 2, 128, 96, BF16, p(2), 1 << 20, None) == 3
+    assert lib.fa_bwd_preprocess(p(0), p(1), 1, 2, 128, 64, BF16, p(2), 1023, None) == 6
+    assert lib.fa_bwd_preprocess(p(0), p(1), 1, 2, 128, 64, BF16, p(1, 64), 1 << 20, None) == 9
+    # dkdv: (Q, K, V, dO, LSE, dK, dV, B, H, N, d, scale, causal, mask, dtype, ws, wsb, stream)
+    args = [p(0), p(1), p(2), p(3), p(4), p(5), p(6), 1, 2, 128, 64, 0.125, 0, None, BF16, p(7),
+            1 << 20, None]
+    bad = list(args); bad[5] = None
+    assert lib.fa_bwd_dkdv(*bad) == 1
+    bad = list(args); bad[16] = 4
+    assert lib.fa_bwd_dkdv(*bad) == 6
+    bad = list(args); bad[6] = p(7)            # dV over the workspace (read by the pass)
+    assert lib.fa_bwd_dkdv(*bad) == 9
+    bad = list(args); bad[11] = -1.0
+    assert lib.fa_bwd_dkdv(*bad) == 8
+    # dq: (Q, K, V, dO, LSE, dQ, B, H, N, d, scale, causal, mask, dtype, ws, wsb, stream)
+    args = [p(0), p(1), p(2), p(3), p(4), p(5), 1, 2, 128, 64, 0.125, 1, None, BF16, p(7),
+            1 << 20, None]
+    bad = list(args); bad[5] = p(0, 16)
+    assert lib.fa_bwd_dq(*bad) == 9
+    bad = list(args); bad[14] = None
+    assert lib.fa_bwd_dq(*bad) == 6
+    bad = list(args); bad[13] = 3
+    assert lib.fa_bwd_dq(*bad) == 4
+
+
+def test_single_hip_runtime_in_process(lib):
+    """libfa.so binds to the HIP runtime torch already mapped (one copy)."""
+    maps = open("/proc/self/maps").read()
+    paths = {ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln}
+    assert len(paths) == 1, paths
