@@ -110,12 +110,18 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   const int kw = k0 + 32 * w;            // this wave's first key
   const int krow = kw + l32;             // this lane's key
 
-  // K and V rows of this lane as B operands (natural d order).
+  constexpr uint32_t RB = D * sizeof(T);
+
+  // K and V rows of this lane as B operands (natural d order); rows past N
+  // read as zero.
+  const rsrc_t rk = make_rsrc(K + head, (uint32_t)N * RB);
+  const rsrc_t rv = make_rsrc(V + head, (uint32_t)N * RB);
   frag kf[NT], vf[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    kf[t] = krow < N ? E::load(K + head + (size_t)krow * D + 16 * t + 8 * g) : E::zero();
-    vf[t] = krow < N ? E::load(V + head + (size_t)krow * D + 16 * t + 8 * g) : E::zero();
+    const uint32_t off = (uint32_t)krow * RB + (16 * t + 8 * g) * sizeof(T);
+    kf[t] = gload_frag<T>(rk, off);
+    vf[t] = gload_frag<T>(rv, off);
   }
 
   const int ntiles = (N + BQ - 1) / BQ;
@@ -128,24 +134,30 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
     return i;
   };
 
+  const rsrc_t rl = make_rsrc(Lh, (uint32_t)N * 4);
+  const rsrc_t rd = make_rsrc(Dh, (uint32_t)N * 4);
   QuadTask<T, D> qt[TPT], ot[TPT];
   float lpre = 0.f, dpre = 0.f;
+  int lrow_pre = 0;
   auto load_tile = [&](int i) {
     const int q0 = i * BQ;
+    const uint32_t left = (uint32_t)(N - q0) * RB;
+    const rsrc_t rq = make_rsrc(Qh + (size_t)q0 * D, left);
+    const rsrc_t ro = make_rsrc(dOh + (size_t)q0 * D, left);
 #pragma unroll
     for (int x = 0; x < TPT; ++x) {
       const int task = tid + x * kThreads;
       if (task < TASKS) {
-        const int rq = task / (D / CH), col = (task % (D / CH)) * CH;
-        qt[x].load(Qh + (size_t)q0 * D, 4 * rq, col, N - q0);
-        ot[x].load(dOh + (size_t)q0 * D, 4 * rq, col, N - q0);
+        const int rq4 = task / (D / CH), col = (task % (D / CH)) * CH;
+        const uint32_t off = (uint32_t)(4 * rq4) * RB + col * sizeof(T);
+        qt[x].load(rq, off);
+        ot[x].load(ro, off);
       }
     }
     if (tid < BQ) {
-      const int q = q0 + tid;
-      const float l = q < N ? Lh[q] : neg_inf();
-      lpre = l == neg_inf() ? pos_inf() : l * kLog2e;
-      dpre = q < N ? Dh[q] : 0.f;
+      lpre = buf_load_f32(rl, (uint32_t)(q0 + tid) * 4);   // raw; used at store time
+      dpre = buf_load_f32(rd, (uint32_t)(q0 + tid) * 4);
+      lrow_pre = q0 + tid;
     }
   };
   auto store_tile = [&]() {
@@ -160,7 +172,11 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
         ot[x].store_transposed(sdOt, LDT, 4 * rq, col);
       }
     }
-    if (tid < BQ) { sL[tid] = lpre; sD[tid] = dpre; }
+    if (tid < BQ) {
+      // Rows past N, and rows that keep no key (LSE = -inf), get P = 0.
+      sL[tid] = (lrow_pre < N && lpre != neg_inf()) ? lpre * kLog2e : pos_inf();
+      sD[tid] = dpre;
+    }
   };
 
   f32x16 dkacc[ND], dvacc[ND];
@@ -170,6 +186,7 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   int i = next_kept(first);
   if (i < ntiles) load_tile(i);
   while (i < ntiles) {
+    wait_global_loads();
     __syncthreads();
     store_tile();
     __syncthreads();
@@ -284,18 +301,20 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   const T* Vh = V + head;
   const int qrow = q0 + 32 * w + l32;
 
+  constexpr uint32_t RB = D * sizeof(T);
+  const rsrc_t rq = make_rsrc(Q + head, (uint32_t)N * RB);
+  const rsrc_t ro = make_rsrc(dO + head, (uint32_t)N * RB);
   frag qf[NT], of[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    qf[t] = qrow < N ? E::load(Q + head + (size_t)qrow * D + 16 * t + 8 * g) : E::zero();
-    of[t] = qrow < N ? E::load(dO + head + (size_t)qrow * D + 16 * t + 8 * g) : E::zero();
+    const uint32_t off = (uint32_t)qrow * RB + (16 * t + 8 * g) * sizeof(T);
+    qf[t] = gload_frag<T>(rq, off);
+    of[t] = gload_frag<T>(ro, off);
   }
-  float lse2 = pos_inf(), dval = 0.f;
-  if (qrow < N) {
-    const float l = LSE[(size_t)bh * N + qrow];
-    lse2 = l == neg_inf() ? pos_inf() : l * kLog2e;
-    dval = delta[(size_t)bh * N + qrow];
-  }
+  // Rows past N, and rows that keep no key (LSE = -inf), get P = 0.
+  const float lrow = buf_load_f32(make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4), (uint32_t)qrow * 4);
+  const float lse2 = (qrow < N && lrow != neg_inf()) ? lrow * kLog2e : pos_inf();
+  const float dval = buf_load_f32(make_rsrc(delta + (size_t)bh * N, (uint32_t)N * 4), (uint32_t)qrow * 4);
 
   const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
   const int ntiles = (kv_end + BC - 1) / BC;
@@ -310,13 +329,17 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   QuadTask<T, D> kt[TPT], vt[TPT];
   auto load_tile = [&](int j) {
     const int kv0 = j * BC;
+    const uint32_t left = (uint32_t)(N - kv0) * RB;
+    const rsrc_t rk = make_rsrc(Kh + (size_t)kv0 * D, left);
+    const rsrc_t rv = make_rsrc(Vh + (size_t)kv0 * D, left);
 #pragma unroll
     for (int x = 0; x < TPT; ++x) {
       const int task = tid + x * kThreads;
       if (task < TASKS) {
-        const int rq = task / (D / CH), col = (task % (D / CH)) * CH;
-        kt[x].load(Kh + (size_t)kv0 * D, 4 * rq, col, N - kv0);
-        vt[x].load(Vh + (size_t)kv0 * D, 4 * rq, col, N - kv0);
+        const int rq4 = task / (D / CH), col = (task % (D / CH)) * CH;
+        const uint32_t off = (uint32_t)(4 * rq4) * RB + col * sizeof(T);
+        kt[x].load(rk, off);
+        vt[x].load(rv, off);
       }
     }
   };
@@ -340,6 +363,7 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   int j = next_kept(0);
   if (j < ntiles) load_tile(j);
   while (j < ntiles) {
+    wait_global_loads();
     __syncthreads();
     store_tile();
     __syncthreads();
@@ -358,13 +382,12 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
         const frag av = E::load(sV + (32 * h + l32) * LDR + 16 * t + 8 * g);
         dp = E::mma(av, of[t], dp);
       }
+      // Register r holds key kv0 + 4g + 32h + 8(r/4) + r%4.
+      const int lim = (CAUSAL ? min(N, qrow + 1) : N) - kv0 - 4 * g - 32 * h;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
-        if (need_mask) {
-          const int kv = kv0 + 32 * h + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (kv >= N || (CAUSAL && kv > qrow)) p = 0.f;
-        }
+        if (need_mask && 8 * (r >> 2) + (r & 3) >= lim) p = 0.f;
         dp[r] = p * (dp[r] - dval);
       }
 #pragma unroll
@@ -413,7 +436,7 @@ static hipError_t launch_dkdv_t(const BwdArgs& a) {
                      dim3(kThreads), 0, a.stream, static_cast<const T*>(a.q),
                      static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                      static_cast<const T*>(a.dout), a.lse, a.delta, static_cast<T*>(a.dk),
-                     static_cast<T*>(a.dv), a.mask, a.BH, a.N, a.T, a.scale * kLog2e, a.scale);
+                     static_cast<T*>(a.dv), a.mask, a.BH, a.N, a.T, score_coef(a.scale), a.scale);
   return hipGetLastError();
 }
 
@@ -423,7 +446,7 @@ static hipError_t launch_dq_t(const BwdArgs& a) {
   hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, CAUSAL, MASKED>), dim3(nqb * a.BH), dim3(kThreads),
                      0, a.stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                      static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
-                     static_cast<T*>(a.dq), a.mask, a.BH, a.N, a.T, a.scale * kLog2e, a.scale);
+                     static_cast<T*>(a.dq), a.mask, a.BH, a.N, a.T, score_coef(a.scale), a.scale);
   return hipGetLastError();
 }
 

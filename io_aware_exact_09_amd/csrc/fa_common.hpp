@@ -38,6 +38,15 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaskBlock = 128;
 constexpr int kThreads = 256;   // 4 waves per work-group
 
+// Exponent coefficient c = scale * log2(e), clamped to at least FLT_MIN so
+// that c > 0: a masked score (-inf) then always gives 2^(-inf * c) = 0.  For
+// scale = 0 every kept exponent is 2^(s * FLT_MIN - m) with |s * FLT_MIN| far
+// below half an ulp of 1, i.e. exactly the values scale = 0 gives.
+inline float score_coef(float scale) {
+  const float c = scale * kLog2e;
+  return c < 1.17549435e-38f ? 1.17549435e-38f : c;
+}
+
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 __device__ __forceinline__ float pos_inf() { return __builtin_inff(); }
 
@@ -108,25 +117,61 @@ template <> struct Elem<float> {
 };
 
 // ---------------------------------------------------------------------------
+// Global loads through raw buffer descriptors.  A descriptor covers [base,
+// base + bytes); a load whose offset falls outside returns zeros, so tile
+// tails need no branches (and the waitcnt bookkeeping of the loads stays
+// exact, which a branch around each load would defeat).
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// Wait until every outstanding global load of this wave has landed
+// (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maximum).  Issued
+// unconditionally at the top of each tile iteration: the LDS stores need the
+// prefetched tile anyway, and it tells the compiler that older loads (the
+// fragments loaded before the loop) are complete.
+__device__ __forceinline__ void wait_global_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// One operand fragment (8 contraction values) read straight from global memory.
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::frag gload_frag(rsrc_t r, uint32_t off) {
+  typename Elem<T>::frag f;
+  if constexpr (sizeof(T) == 2) {
+    f.v = __builtin_bit_cast(bf16x8, buf_load16(r, off));
+  } else {
+    f.lo = __builtin_bit_cast(f32x4, buf_load16(r, off));
+    f.hi = __builtin_bit_cast(f32x4, buf_load16(r, off + 16));
+  }
+  return f;
+}
+
+// ---------------------------------------------------------------------------
 // Tile staging: global [rows x D] row-major (row stride D) -> LDS.
 //
 // A "quad task" covers 4 consecutive rows x one 16-byte column chunk.  It is
-// loaded with four 16-byte global loads (rows past `valid` read as zero) and
-// can be written to LDS row-major and/or transposed (contraction-permuted).
+// loaded with four 16-byte buffer loads (rows outside the descriptor read as
+// zero) and can be written to LDS row-major and/or transposed
+// (contraction-permuted).
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 struct QuadTask {
   static constexpr int E = Elem<T>::kPerChunk;   // elements per chunk
+  static constexpr uint32_t kRowBytes = D * sizeof(T);
   u32x4 r[4];
 
-  __device__ void load(const T* base, int row0, int col, int valid) {
+  // `off`: byte offset, inside the descriptor, of (row0, col).
+  __device__ void load(rsrc_t rs, uint32_t off) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (row0 + i < valid)
-        r[i] = *reinterpret_cast<const u32x4*>(base + (size_t)(row0 + i) * D + col);
-      else
-        r[i] = u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < 4; ++i) r[i] = buf_load16(rs, off + i * kRowBytes);
   }
   // Row-major: lds[(row0+i) * ld + col .. +E]
   __device__ void store_rows(T* lds, int ld, int row0, int col) const {
@@ -141,7 +186,7 @@ struct QuadTask {
 template <typename T, int D>
 __device__ __forceinline__ void QuadTask<T, D>::store_transposed(T* ldsT, int ldt, int row0,
                                                                  int col) const {
-  const int p = (row0 & ~15) | perm16(row0 & 15);
+  const int p = perm16(row0);
   if constexpr (sizeof(T) == 2) {
     // r[i] holds 8 bf16 of row i: element e sits in dword e/2, half e%2.
 #pragma unroll

@@ -66,16 +66,18 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   const BlockCoord bc = map_block(blockIdx.x, nqb, BH, CAUSAL, true);
   const int bh = bc.bh, q0 = bc.blk * BR;
   const size_t head = (size_t)bh * N * D;
-  const T* Qh = Q + head;
   const T* Kh = K + head;
   const T* Vh = V + head;
   const int qrow = q0 + 32 * w + l32;
+  constexpr uint32_t RB = D * sizeof(T);       // bytes per row
 
-  // Query fragments (B operand, natural order): Q[qrow][16t + 8g .. +7].
+  // Query fragments (B operand, natural order): Q[qrow][16t + 8g .. +7];
+  // rows past N read as zero.
+  const rsrc_t rq = make_rsrc(Q + head, (uint32_t)N * RB);
   frag qf[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
-    qf[t] = qrow < N ? E::load(Qh + (size_t)qrow * D + 16 * t + 8 * g) : E::zero();
+    qf[t] = gload_frag<T>(rq, (uint32_t)qrow * RB + (16 * t + 8 * g) * sizeof(T));
 
   const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
   const int ntiles = (kv_end + BC - 1) / BC;
@@ -90,20 +92,23 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   QuadTask<T, D> kt[KPT], vt[VPT];
   auto load_tile = [&](int j) {
     const int kv0 = j * BC;
+    const uint32_t left = (uint32_t)(N - kv0) * RB;
+    const rsrc_t rk = make_rsrc(Kh + (size_t)kv0 * D, left);
+    const rsrc_t rv = make_rsrc(Vh + (size_t)kv0 * D, left);
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int task = tid + i * kThreads;
       if (task < KTASKS) {
-        const int rq = task / (D / CH), col = (task % (D / CH)) * CH;
-        kt[i].load(Kh + (size_t)kv0 * D, 4 * rq, col, N - kv0);
+        const int rq4 = task / (D / CH), col = (task % (D / CH)) * CH;
+        kt[i].load(rk, (uint32_t)(4 * rq4) * RB + col * sizeof(T));
       }
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int task = tid + i * kThreads;
       if (task < VTASKS) {
-        const int rq = task / (D / CH), col = (task % (D / CH)) * CH;
-        vt[i].load(Vh + (size_t)kv0 * D, 4 * rq, col, N - kv0);
+        const int rq4 = task / (D / CH), col = (task % (D / CH)) * CH;
+        vt[i].load(rv, (uint32_t)(4 * rq4) * RB + col * sizeof(T));
       }
     }
   };
@@ -135,6 +140,7 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   int j = next_kept(0);
   if (j < ntiles) load_tile(j);
   while (j < ntiles) {
+    wait_global_loads();
     __syncthreads();                 // everyone is done reading the previous tile
     store_tile();
     __syncthreads();
@@ -155,29 +161,28 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     }
 
     // ---- mask (diagonal / tail tiles only) -------------------------------
+    // Register r of half h holds key kv0 + 4g + off, off = 32h + 8(r/4) + r%4;
+    // it is kept iff off < lim.
     const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > q0 + 32 * w);
-    uint32_t keep_bits = 0xffffffffu;
     if (need_mask) {
-      keep_bits = 0;
+      const int lim = (CAUSAL ? min(N, qrow + 1) : N) - kv0 - 4 * g;
 #pragma unroll
       for (int h = 0; h < NH; ++h)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kv = kv0 + 32 * h + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool keep = kv < N && (!CAUSAL || kv <= qrow);
-          keep_bits |= (keep ? 1u : 0u) << (16 * h + r);
-          if (!keep) s[h][r] = neg_inf();
-        }
+        for (int r = 0; r < 16; ++r)
+          if (32 * h + 8 * (r >> 2) + (r & 3) >= lim) s[h][r] = neg_inf();
     }
 
     // ---- online softmax ----------------------------------------------------
+    // c > 0 (the host clamps it to at least FLT_MIN), so a masked score gives
+    // 2^(-inf) = 0 and the row max of kept scores times c is the max of S*c.
     float mx = neg_inf();
 #pragma unroll
     for (int h = 0; h < NH; ++h)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[h][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_tile = mx == neg_inf() ? neg_inf() : mx * c;
+    const float m_tile = mx * c;
     const float m_new = fmaxf(m_run, m_tile);
     const float m_use = m_new == neg_inf() ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);   // 0 while m_run = -inf
@@ -186,8 +191,7 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     for (int h = 0; h < NH; ++h)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(fmaf(s[h][r], c, -m_use));
-        if (need_mask && !((keep_bits >> (16 * h + r)) & 1u)) p = 0.f;
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[h][r], c, -m_use));
         s[h][r] = p;
         psum += p;
       }
@@ -239,7 +243,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
   hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, MASKED>), grid, block, 0, a.stream,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                      static_cast<const T*>(a.v), static_cast<T*>(a.o), a.lse, a.mask, a.BH,
-                     a.N, a.T, a.scale * kLog2e);
+                     a.N, a.T, score_coef(a.scale));
   return hipGetLastError();
 }
 
