@@ -15,7 +15,9 @@
 // Three kernels run in order on one stream:
 //   1. fa_bwd_delta: D = rowsum(dO * O) into the caller's workspace.
 //   2. fa_bwd_dkdv:  one work-group per 128 keys; walks the kept query tiles,
-//                    accumulates dK, dV on chip, writes them once.
+//                    accumulates dK, dV on chip, writes them once.  Q and dO
+//                    tiles are staged row-major; their transposes are read
+//                    with the transposing LDS load.
 //   3. fa_bwd_dq:    one work-group per 128 queries; walks the kept key tiles,
 //                    accumulates dQ on chip, writes it once.
 // Splitting dQ into its own pass recomputes S and dP once more but needs no
@@ -60,14 +62,13 @@ fa_bwd_delta_kernel(const T* __restrict__ O, const T* __restrict__ dO, float* __
 //      S   = Q_i K_j^T      (A = Q rows from LDS, B = K in registers)
 //      dP  = dO_i V_j^T     (A = dO rows from LDS, B = V in registers)
 //      P, dS elementwise in the C layout (query index per register)
-//      dV^T += dO_i^T P     (A = dO^T from LDS, B = P registers)
-//      dK^T += Q_i^T dS     (A = Q^T from LDS,  B = dS registers)
+//      dV^T += dO_i^T P     (A = dO^T by transposing LDS reads, B = P registers)
+//      dK^T += Q_i^T dS     (A = Q^T by transposing LDS reads, B = dS registers)
 // ---------------------------------------------------------------------------
 template <typename T>
 struct DkdvCfg {
   static constexpr int BK = 128;                         // keys per work-group
   static constexpr int BQ = sizeof(T) == 2 ? 64 : 32;   // query rows per tile
-  static constexpr int PAD = 16 / sizeof(T);
 };
 
 template <typename T, int D, bool CAUSAL, bool MASKED>
@@ -81,21 +82,16 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   using E = Elem<T>;
   using frag = typename E::frag;
   using Cfg = DkdvCfg<T>;
-  constexpr int BK = Cfg::BK, BQ = Cfg::BQ, PAD = Cfg::PAD;
+  constexpr int BK = Cfg::BK, BQ = Cfg::BQ;
   constexpr int NQH = BQ / 32;            // 32-row query halves per tile
   constexpr int NT = D / 16, ND = D / 32;
-  constexpr int LDR = D + PAD;            // row-major tiles
-  constexpr int LDT = BQ + PAD;           // transposed tiles
-  constexpr int CH = E::kPerChunk;
-  constexpr int TASKS = (BQ / 4) * (D / CH);
-  constexpr int TPT = (TASKS + kThreads - 1) / kThreads;
+  constexpr uint32_t RB = Tile<T, D>::RB;
+  constexpr int TB = BQ * RB;             // bytes per Q or dO tile
 
-  __shared__ __attribute__((aligned(16))) T sQ[BQ * LDR];
-  __shared__ __attribute__((aligned(16))) T sdO[BQ * LDR];
-  __shared__ __attribute__((aligned(16))) T sQt[D * LDT];
-  __shared__ __attribute__((aligned(16))) T sdOt[D * LDT];
-  __shared__ __attribute__((aligned(16))) float sL[BQ];   // LSE * log2e (+inf: no keys / pad)
-  __shared__ __attribute__((aligned(16))) float sD[BQ];
+  // [buffer][Q, dO] tiles, double-buffered, plus per-row LSE*log2e and D.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * TB];
+  __shared__ __attribute__((aligned(16))) float sL[2][BQ];   // +inf: no keys / past N
+  __shared__ __attribute__((aligned(16))) float sD[2][BQ];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
@@ -105,12 +101,8 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   const size_t head = (size_t)bh * N * D;
   const T* Qh = Q + head;
   const T* dOh = dO + head;
-  const float* Lh = LSE + (size_t)bh * N;
-  const float* Dh = delta + (size_t)bh * N;
   const int kw = k0 + 32 * w;            // this wave's first key
   const int krow = kw + l32;             // this lane's key
-
-  constexpr uint32_t RB = D * sizeof(T);
 
   // K and V rows of this lane as B operands (natural d order); rows past N
   // read as zero.
@@ -134,48 +126,20 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
     return i;
   };
 
-  const rsrc_t rl = make_rsrc(Lh, (uint32_t)N * 4);
-  const rsrc_t rd = make_rsrc(Dh, (uint32_t)N * 4);
-  QuadTask<T, D> qt[TPT], ot[TPT];
-  float lpre = 0.f, dpre = 0.f;
+  const rsrc_t rl = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
+  const rsrc_t rd = make_rsrc(delta + (size_t)bh * N, (uint32_t)N * 4);
+  float lpre = 0.f, dpre = 0.f;     // row statistics of the tile in flight (threads < BQ)
   int lrow_pre = 0;
-  auto load_tile = [&](int i) {
+  auto stage = [&](int i, int buf) {
     const int q0 = i * BQ;
     const uint32_t left = (uint32_t)(N - q0) * RB;
-    const rsrc_t rq = make_rsrc(Qh + (size_t)q0 * D, left);
-    const rsrc_t ro = make_rsrc(dOh + (size_t)q0 * D, left);
-#pragma unroll
-    for (int x = 0; x < TPT; ++x) {
-      const int task = tid + x * kThreads;
-      if (task < TASKS) {
-        const int rq4 = task / (D / CH), col = (task % (D / CH)) * CH;
-        const uint32_t off = (uint32_t)(4 * rq4) * RB + col * sizeof(T);
-        qt[x].load(rq, off);
-        ot[x].load(ro, off);
-      }
-    }
+    unsigned char* base = smem + buf * 2 * TB;
+    stage_tile<T, D, BQ>(make_rsrc(Qh + (size_t)q0 * D, left), base, w, lane);
+    stage_tile<T, D, BQ>(make_rsrc(dOh + (size_t)q0 * D, left), base + TB, w, lane);
     if (tid < BQ) {
-      lpre = buf_load_f32(rl, (uint32_t)(q0 + tid) * 4);   // raw; used at store time
+      lpre = buf_load_f32(rl, (uint32_t)(q0 + tid) * 4);   // raw; transformed when stored
       dpre = buf_load_f32(rd, (uint32_t)(q0 + tid) * 4);
       lrow_pre = q0 + tid;
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int x = 0; x < TPT; ++x) {
-      const int task = tid + x * kThreads;
-      if (task < TASKS) {
-        const int rq = task / (D / CH), col = (task % (D / CH)) * CH;
-        qt[x].store_rows(sQ, LDR, 4 * rq, col);
-        qt[x].store_transposed(sQt, LDT, 4 * rq, col);
-        ot[x].store_rows(sdO, LDR, 4 * rq, col);
-        ot[x].store_transposed(sdOt, LDT, 4 * rq, col);
-      }
-    }
-    if (tid < BQ) {
-      // Rows past N, and rows that keep no key (LSE = -inf), get P = 0.
-      sL[tid] = (lrow_pre < N && lpre != neg_inf()) ? lpre * kLog2e : pos_inf();
-      sD[tid] = dpre;
     }
   };
 
@@ -184,15 +148,21 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   for (int b = 0; b < ND; ++b) { dkacc[b] = f32x16{}; dvacc[b] = f32x16{}; }
 
   int i = next_kept(first);
-  if (i < ntiles) load_tile(i);
+  int buf = 0;
+  if (i < ntiles) stage(i, 0);
   while (i < ntiles) {
     wait_global_loads();
-    __syncthreads();
-    store_tile();
+    if (tid < BQ) {
+      // Rows past N, and rows that keep no key (LSE = -inf), get P = 0.
+      sL[buf][tid] = (lrow_pre < N && lpre != neg_inf()) ? lpre * kLog2e : pos_inf();
+      sD[buf][tid] = dpre;
+    }
     __syncthreads();
     const int q0 = i * BQ;
     const int in = next_kept(i + 1);
-    if (in < ntiles) load_tile(in);
+    if (in < ntiles) stage(in, buf ^ 1);
+    const unsigned char* sQ = smem + buf * 2 * TB;
+    const unsigned char* sdO = sQ + TB;
 
     const bool need_mask = CAUSAL && (q0 < kw + 31);
 #pragma unroll
@@ -200,17 +170,15 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const frag aq = E::load(sQ + (32 * qh + l32) * LDR + 16 * t + 8 * g);
-        s = E::mma(aq, kf[t], s);
-        const frag ao = E::load(sdO + (32 * qh + l32) * LDR + 16 * t + 8 * g);
-        dp = E::mma(ao, vf[t], dp);
+        s = E::mma(row_frag<T, D>(sQ, 32 * qh + l32, t, g), kf[t], s);
+        dp = E::mma(row_frag<T, D>(sdO, 32 * qh + l32, t, g), vf[t], dp);
       }
       // Register r holds query 32qh + 8(r/4) + 4g + r%4 of this tile.
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int qi = 32 * qh + 8 * a + 4 * g;
-        const f32x4 lv = *reinterpret_cast<const f32x4*>(sL + qi);
-        const f32x4 dv = *reinterpret_cast<const f32x4*>(sD + qi);
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(&sL[buf][qi]);
+        const f32x4 dv = *reinterpret_cast<const f32x4*>(&sD[buf][qi]);
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int r = 4 * a + x;
@@ -227,13 +195,12 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
         const int cc = 2 * qh + t;      // 16-row chunk of the query tile
 #pragma unroll
         for (int b = 0; b < ND; ++b) {
-          const frag ao = E::load(sdOt + (32 * b + l32) * LDT + 16 * cc + 8 * g);
-          dvacc[b] = E::mma(ao, pf, dvacc[b]);
-          const frag aq = E::load(sQt + (32 * b + l32) * LDT + 16 * cc + 8 * g);
-          dkacc[b] = E::mma(aq, df, dkacc[b]);
+          dvacc[b] = E::mma(trans_frag<T, D>(sdO, b, cc, lane), pf, dvacc[b]);
+          dkacc[b] = E::mma(trans_frag<T, D>(sQ, b, cc, lane), df, dkacc[b]);
         }
       }
     }
+    buf ^= 1;
     i = in;
   }
 
@@ -260,13 +227,12 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
 //      S^T  = K_j Q_i^T     (A = K rows from LDS, B = Q registers)
 //      dP^T = V_j dO_i^T    (A = V rows from LDS, B = dO registers)
 //      P^T, dS^T elementwise with this lane's own LSE_i and D_i
-//      dQ^T += K_j^T dS^T   (A = K^T from LDS, B = dS^T registers)
+//      dQ^T += K_j^T dS^T   (A = K^T via transposing LDS reads, B = dS^T)
 // ---------------------------------------------------------------------------
 template <typename T>
 struct DqCfg {
   static constexpr int BR = 128;
   static constexpr int BC = sizeof(T) == 2 ? 64 : 32;
-  static constexpr int PAD = 16 / sizeof(T);
 };
 
 template <typename T, int D, bool CAUSAL, bool MASKED>
@@ -280,16 +246,12 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   using E = Elem<T>;
   using frag = typename E::frag;
   using Cfg = DqCfg<T>;
-  constexpr int BR = Cfg::BR, BC = Cfg::BC, PAD = Cfg::PAD;
+  constexpr int BR = Cfg::BR, BC = Cfg::BC;
   constexpr int NH = BC / 32, NT = D / 16, ND = D / 32;
-  constexpr int LDR = D + PAD, LDT = BC + PAD;
-  constexpr int CH = E::kPerChunk;
-  constexpr int TASKS = (BC / 4) * (D / CH);
-  constexpr int TPT = (TASKS + kThreads - 1) / kThreads;
+  constexpr uint32_t RB = Tile<T, D>::RB;
+  constexpr int TB = BC * RB;
 
-  __shared__ __attribute__((aligned(16))) T sK[BC * LDR];
-  __shared__ __attribute__((aligned(16))) T sV[BC * LDR];
-  __shared__ __attribute__((aligned(16))) T sKt[D * LDT];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * TB];   // [buf][K, V]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
@@ -301,7 +263,6 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   const T* Vh = V + head;
   const int qrow = q0 + 32 * w + l32;
 
-  constexpr uint32_t RB = D * sizeof(T);
   const rsrc_t rq = make_rsrc(Q + head, (uint32_t)N * RB);
   const rsrc_t ro = make_rsrc(dO + head, (uint32_t)N * RB);
   frag qf[NT], of[NT];
@@ -313,7 +274,6 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   }
   // Rows past N, and rows that keep no key (LSE = -inf), get P = 0.
   const float lrow = buf_load_f32(make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4), (uint32_t)qrow * 4);
-  const float lse2 = (qrow < N && lrow != neg_inf()) ? lrow * kLog2e : pos_inf();
   const float dval = buf_load_f32(make_rsrc(delta + (size_t)bh * N, (uint32_t)N * 4), (uint32_t)qrow * 4);
 
   const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
@@ -325,35 +285,12 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
     }
     return j;
   };
-
-  QuadTask<T, D> kt[TPT], vt[TPT];
-  auto load_tile = [&](int j) {
+  auto stage = [&](int j, int buf) {
     const int kv0 = j * BC;
     const uint32_t left = (uint32_t)(N - kv0) * RB;
-    const rsrc_t rk = make_rsrc(Kh + (size_t)kv0 * D, left);
-    const rsrc_t rv = make_rsrc(Vh + (size_t)kv0 * D, left);
-#pragma unroll
-    for (int x = 0; x < TPT; ++x) {
-      const int task = tid + x * kThreads;
-      if (task < TASKS) {
-        const int rq4 = task / (D / CH), col = (task % (D / CH)) * CH;
-        const uint32_t off = (uint32_t)(4 * rq4) * RB + col * sizeof(T);
-        kt[x].load(rk, off);
-        vt[x].load(rv, off);
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int x = 0; x < TPT; ++x) {
-      const int task = tid + x * kThreads;
-      if (task < TASKS) {
-        const int rq = task / (D / CH), col = (task % (D / CH)) * CH;
-        kt[x].store_rows(sK, LDR, 4 * rq, col);
-        kt[x].store_transposed(sKt, LDT, 4 * rq, col);
-        vt[x].store_rows(sV, LDR, 4 * rq, col);
-      }
-    }
+    unsigned char* base = smem + buf * 2 * TB;
+    stage_tile<T, D, BC>(make_rsrc(Kh + (size_t)kv0 * D, left), base, w, lane);
+    stage_tile<T, D, BC>(make_rsrc(Vh + (size_t)kv0 * D, left), base + TB, w, lane);
   };
 
   f32x16 dqacc[ND];
@@ -361,15 +298,18 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   for (int b = 0; b < ND; ++b) dqacc[b] = f32x16{};
 
   int j = next_kept(0);
-  if (j < ntiles) load_tile(j);
+  int buf = 0;
+  if (j < ntiles) stage(j, 0);
+  wait_global_loads();
+  const float lse2 = (qrow < N && lrow != neg_inf()) ? lrow * kLog2e : pos_inf();
   while (j < ntiles) {
     wait_global_loads();
     __syncthreads();
-    store_tile();
-    __syncthreads();
     const int kv0 = j * BC;
     const int jn = next_kept(j + 1);
-    if (jn < ntiles) load_tile(jn);
+    if (jn < ntiles) stage(jn, buf ^ 1);
+    const unsigned char* sK = smem + buf * 2 * TB;
+    const unsigned char* sV = sK + TB;
 
     const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > q0 + 32 * w);
 #pragma unroll
@@ -377,10 +317,8 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const frag ak = E::load(sK + (32 * h + l32) * LDR + 16 * t + 8 * g);
-        s = E::mma(ak, qf[t], s);
-        const frag av = E::load(sV + (32 * h + l32) * LDR + 16 * t + 8 * g);
-        dp = E::mma(av, of[t], dp);
+        s = E::mma(row_frag<T, D>(sK, 32 * h + l32, t, g), qf[t], s);
+        dp = E::mma(row_frag<T, D>(sV, 32 * h + l32, t, g), of[t], dp);
       }
       // Register r holds key kv0 + 4g + 32h + 8(r/4) + r%4.
       const int lim = (CAUSAL ? min(N, qrow + 1) : N) - kv0 - 4 * g - 32 * h;
@@ -395,12 +333,11 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
         const frag df = E::from_c(dp, t);
         const int cc = 2 * h + t;
 #pragma unroll
-        for (int b = 0; b < ND; ++b) {
-          const frag a = E::load(sKt + (32 * b + l32) * LDT + 16 * cc + 8 * g);
-          dqacc[b] = E::mma(a, df, dqacc[b]);
-        }
+        for (int b = 0; b < ND; ++b)
+          dqacc[b] = E::mma(trans_frag<T, D>(sK, b, cc, lane), df, dqacc[b]);
       }
     }
+    buf ^= 1;
     j = jn;
   }
 

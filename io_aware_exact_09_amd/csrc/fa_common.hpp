@@ -155,59 +155,119 @@ __device__ __forceinline__ typename Elem<T>::frag gload_frag(rsrc_t r, uint32_t 
 }
 
 // ---------------------------------------------------------------------------
-// Tile staging: global [rows x D] row-major (row stride D) -> LDS.
+// LDS tiles.
 //
-// A "quad task" covers 4 consecutive rows x one 16-byte column chunk.  It is
-// loaded with four 16-byte buffer loads (rows outside the descriptor read as
-// zero) and can be written to LDS row-major and/or transposed
-// (contraction-permuted).
+// A tile holds R rows of a [*, D] row-major tensor, unpadded (D * sizeof(T)
+// bytes per row), with the 16-byte chunks of row r stored at chunk position
+// c ^ swz(r).  The swizzles were chosen against the gfx950 LDS, which serves
+// ds_read_b128 16 lanes (256 bytes) at a time and ds_read_b64_tr_b16 32 lanes
+// at a time:
+//   * operand reads along a row (ds_read_b128 by 16 consecutive rows at one
+//     chunk) need swz to be a bijection over 16 consecutive rows;
+//   * transposed reads (ds_read_b64_tr_b16: 4 consecutive rows x 64 bytes per
+//     32 lanes) need those 4 rows to land in 4 different 64-byte segments of
+//     the 256-byte bank window.
+// bf16, D = 128: swz(r) = 4 (r % 4) + (r / 4) % 4 satisfies both; bf16, D = 64
+// (two rows per bank window): swz(r) = 4 ((r / 2) % 2) + (r / 4) % 4.  The
+// fp32 path reads transposed operands with scalar loads and uses r % 16.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-struct QuadTask {
-  static constexpr int E = Elem<T>::kPerChunk;   // elements per chunk
-  static constexpr uint32_t kRowBytes = D * sizeof(T);
-  u32x4 r[4];
-
-  // `off`: byte offset, inside the descriptor, of (row0, col).
-  __device__ void load(rsrc_t rs, uint32_t off) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = buf_load16(rs, off + i * kRowBytes);
+struct Tile {
+  static constexpr int RB = D * (int)sizeof(T);    // bytes per row
+  __device__ static constexpr int swz(int r) {
+    if constexpr (sizeof(T) == 2) {
+      if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+      else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    } else {
+      return r & 15;
+    }
   }
-  // Row-major: lds[(row0+i) * ld + col .. +E]
-  __device__ void store_rows(T* lds, int ld, int row0, int col) const {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(lds + (row0 + i) * ld + col) = r[i];
+  // Byte offset of logical 16-byte chunk c of row r.
+  __device__ static constexpr uint32_t off(int r, int c) {
+    return (uint32_t)(r * RB + ((c ^ swz(r)) << 4));
   }
-  // Transposed: ldsT[(col+e) * ldt + perm16(row0) .. +4]; row0 % 4 == 0.
-  __device__ void store_transposed(T* ldsT, int ldt, int row0, int col) const;
 };
 
-template <typename T, int D>
-__device__ __forceinline__ void QuadTask<T, D>::store_transposed(T* ldsT, int ldt, int row0,
-                                                                 int col) const {
-  const int p = perm16(row0);
-  if constexpr (sizeof(T) == 2) {
-    // r[i] holds 8 bf16 of row i: element e sits in dword e/2, half e%2.
+typedef __attribute__((address_space(3))) unsigned char lds_byte;
+__device__ __forceinline__ lds_byte* as_lds(unsigned char* p) { return (lds_byte*)p; }
+
+// Copy R rows of a row-major global tile into an LDS tile (layout Tile<T, D>)
+// with direct buffer->LDS loads: every lane moves one 16-byte chunk, lane l of
+// a wave landing at LDS byte 16 l of the wave's 1 KiB block, so each lane
+// fetches the global chunk that the swizzle puts there.  `src` starts at the
+// tile's first row; rows outside it arrive as zeros.  Waves take 1 KiB blocks
+// round-robin.  Completion: wait_global_loads() in each wave, then a barrier.
+template <typename T, int D, int R>
+__device__ __forceinline__ void stage_tile(rsrc_t src, unsigned char* tile, int w, int lane) {
+  using L = Tile<T, D>;
+  constexpr int NB = R * L::RB / 1024;
+  static_assert(NB % 4 == 0, "tile must be a multiple of 4 KiB");
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1;
-      uint32_t lo, hi;
-      if (e & 1) {
-        lo = (r[0][w] >> 16) | (r[1][w] & 0xffff0000u);
-        hi = (r[2][w] >> 16) | (r[3][w] & 0xffff0000u);
-      } else {
-        lo = (r[0][w] & 0xffffu) | (r[1][w] << 16);
-        hi = (r[2][w] & 0xffffu) | (r[3][w] << 16);
-      }
-      *reinterpret_cast<u32x2*>(ldsT + (col + e) * ldt + p) = u32x2{lo, hi};
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      *reinterpret_cast<u32x4*>(ldsT + (col + e) * ldt + p) =
-          u32x4{r[0][e], r[1][e], r[2][e], r[3][e]};
+  for (int i = 0; i < NB / 4; ++i) {
+    const int blk = w + 4 * i;
+    const int pos = blk * 1024 + lane * 16;
+    const int r = pos / L::RB, pc = (pos % L::RB) >> 4;
+    const uint32_t goff = (uint32_t)(r * L::RB + ((pc ^ L::swz(r)) << 4));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, as_lds(tile + blk * 1024), 16, goff, 0, 0, 0);
   }
+}
+
+// Natural-order operand: 8 contraction values of row `row` starting at
+// element 16 t + 8 g (A operand of a d-contraction with rows as MFMA rows,
+// or B operand with rows as MFMA columns).
+template <typename T, int D>
+__device__ __forceinline__ typename Elem<T>::frag row_frag(const unsigned char* tile, int row,
+                                                            int t, int g) {
+  using L = Tile<T, D>;
+  typename Elem<T>::frag f;
+  if constexpr (sizeof(T) == 2) {
+    f.v = *reinterpret_cast<const bf16x8*>(tile + L::off(row, 2 * t + g));
+  } else {
+    f.lo = *reinterpret_cast<const f32x4*>(tile + L::off(row, 4 * t + 2 * g));
+    f.hi = *reinterpret_cast<const f32x4*>(tile + L::off(row, 4 * t + 2 * g + 1));
+  }
+  return f;
+}
+
+// C-shaped transposed operand: the A operand of a contraction over the tile's
+// rows, for output rows 32 b .. 32 b + 31 (= tile columns) and contraction
+// rows 16 cc .. 16 cc + 15.  Lane (l32, g) gets, for item e, the element at
+// tile row 16 cc + 8 (e / 4) + 4 g + e % 4, column 32 b + l32.
+//
+// bf16: two ds_read_b64_tr_b16.  Within each 16-lane group the instruction
+// gives lane i element (i % 4) of the 8 bytes read by lane 4 k + i / 4, as
+// its k-th value; so source lane j = 4 k + m reads tile row (base + k),
+// columns 4 m .. 4 m + 3 of the group's 16 columns, and lane i receives
+// column i of those 4 rows.
+template <typename T, int D>
+__device__ __forceinline__ typename Elem<T>::frag trans_frag(const unsigned char* tile, int b,
+                                                              int cc, int lane) {
+  using L = Tile<T, D>;
+  typename Elem<T>::frag f;
+  if constexpr (sizeof(T) == 2) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    const int q = lane >> 4, j = lane & 15;
+    const int col = 32 * b + 16 * (q & 1) + 4 * (j & 3);
+    const int row0 = 16 * cc + 4 * (q >> 1) + (j >> 2);
+    const uint32_t o0 = L::off(row0, col >> 3) + ((col & 7) << 1);
+    const uint32_t o1 = L::off(row0 + 8, col >> 3) + ((col & 7) << 1);
+    lds_byte* t3 = as_lds(const_cast<unsigned char*>(tile));
+    const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(t3 + o0));
+    const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(t3 + o1));
+    const v8i16 x = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+    f.v = __builtin_bit_cast(bf16x8, x);
+  } else {
+    const int l32 = lane & 31, g = lane >> 5;
+    const int col = 32 * b + l32;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r0 = 16 * cc + 4 * g + e;
+      f.lo[e] = *reinterpret_cast<const float*>(tile + L::off(r0, col >> 2) + ((col & 3) << 2));
+      f.hi[e] = *reinterpret_cast<const float*>(tile + L::off(r0 + 8, col >> 2) + ((col & 3) << 2));
+    }
+  }
+  return f;
 }
 
 // ---------------------------------------------------------------------------

@@ -9,7 +9,9 @@
 //   rescale l and O by 2^(m_old - m_new) when the max moved,
 //   O^T += V_j^T P~^T    (MFMA; V stored transposed in LDS, P~ from registers)
 //
-// and writes O = O_acc / l and LSE = (m + log2 l) ln 2 at the end.  This is
+// and writes O = O_acc / l and LSE = (m + log2 l) ln 2 at the end.  K and V
+// tiles go straight from global memory into double-buffered LDS (one barrier
+// per tile); V^T operands are read with the transposing LDS load.  This is
 // the per-block update of the FlashAttention reading guide (xyznot.com/tr/
 // paper/2205.14135, "Yöntem" steps 1-4, with the two-part rule of "Artımsal
 // Softmax Takibi") in its deferred-normalisation form (snula.amonoc.com/
@@ -33,7 +35,6 @@ template <typename T>
 struct FwdCfg {
   static constexpr int BR = 128;                          // query rows per work-group
   static constexpr int BC = sizeof(T) == 2 ? 64 : 32;     // keys per tile
-  static constexpr int PAD = 16 / sizeof(T);              // 16-byte row padding
 };
 
 template <typename T, int D, bool CAUSAL, bool MASKED>
@@ -41,24 +42,19 @@ __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
               T* __restrict__ O, float* __restrict__ LSE, const uint8_t* __restrict__ mask,
-              int BH, int N, int T_tiles, float c /* scale*log2e */) {
+              int BH, int N, int T_tiles, float c /* scale*log2e, > 0 */) {
   using E = Elem<T>;
   using frag = typename E::frag;
   using Cfg = FwdCfg<T>;
-  constexpr int BR = Cfg::BR, BC = Cfg::BC, PAD = Cfg::PAD;
+  constexpr int BR = Cfg::BR, BC = Cfg::BC;
   constexpr int NH = BC / 32;              // 32-key halves per tile
   constexpr int NT = D / 16;               // 16-wide d chunks
   constexpr int ND = D / 32;               // 32-wide d blocks of O^T
-  constexpr int LDK = D + PAD;             // sK row stride (elements)
-  constexpr int LDV = BC + PAD;            // sVt row stride
-  constexpr int CH = E::kPerChunk;         // elements per 16-byte chunk
-  constexpr int KTASKS = (BC / 4) * (D / CH);
-  constexpr int VTASKS = KTASKS;
-  constexpr int KPT = (KTASKS + kThreads - 1) / kThreads;   // tasks per thread
-  constexpr int VPT = (VTASKS + kThreads - 1) / kThreads;
+  constexpr uint32_t RB = Tile<T, D>::RB;  // bytes per row
+  constexpr int TB = BC * RB;              // bytes per K or V tile
 
-  __shared__ __attribute__((aligned(16))) T sK[BC * LDK];
-  __shared__ __attribute__((aligned(16))) T sVt[D * LDV];
+  // [buffer][K, V] tiles, double-buffered.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
@@ -69,7 +65,6 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   const T* Kh = K + head;
   const T* Vh = V + head;
   const int qrow = q0 + 32 * w + l32;
-  constexpr uint32_t RB = D * sizeof(T);       // bytes per row
 
   // Query fragments (B operand, natural order): Q[qrow][16t + 8g .. +7];
   // rows past N read as zero.
@@ -88,47 +83,12 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     }
     return j;
   };
-
-  QuadTask<T, D> kt[KPT], vt[VPT];
-  auto load_tile = [&](int j) {
+  auto stage = [&](int j, int buf) {
     const int kv0 = j * BC;
     const uint32_t left = (uint32_t)(N - kv0) * RB;
-    const rsrc_t rk = make_rsrc(Kh + (size_t)kv0 * D, left);
-    const rsrc_t rv = make_rsrc(Vh + (size_t)kv0 * D, left);
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int task = tid + i * kThreads;
-      if (task < KTASKS) {
-        const int rq4 = task / (D / CH), col = (task % (D / CH)) * CH;
-        kt[i].load(rk, (uint32_t)(4 * rq4) * RB + col * sizeof(T));
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int task = tid + i * kThreads;
-      if (task < VTASKS) {
-        const int rq4 = task / (D / CH), col = (task % (D / CH)) * CH;
-        vt[i].load(rv, (uint32_t)(4 * rq4) * RB + col * sizeof(T));
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int task = tid + i * kThreads;
-      if (task < KTASKS) {
-        const int rq = task / (D / CH), col = (task % (D / CH)) * CH;
-        kt[i].store_rows(sK, LDK, 4 * rq, col);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int task = tid + i * kThreads;
-      if (task < VTASKS) {
-        const int rq = task / (D / CH), col = (task % (D / CH)) * CH;
-        vt[i].store_transposed(sVt, LDV, 4 * rq, col);
-      }
-    }
+    unsigned char* base = smem + buf * 2 * TB;
+    stage_tile<T, D, BC>(make_rsrc(Kh + (size_t)kv0 * D, left), base, w, lane);
+    stage_tile<T, D, BC>(make_rsrc(Vh + (size_t)kv0 * D, left), base + TB, w, lane);
   };
 
   f32x16 oacc[ND];
@@ -138,15 +98,16 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   float l_run = 0.f;         // this lane's partial row sum
 
   int j = next_kept(0);
-  if (j < ntiles) load_tile(j);
+  int buf = 0;
+  if (j < ntiles) stage(j, 0);
   while (j < ntiles) {
-    wait_global_loads();
-    __syncthreads();                 // everyone is done reading the previous tile
-    store_tile();
-    __syncthreads();
+    wait_global_loads();             // this wave's part of tile j has landed
+    __syncthreads();                 // all of tile j is in LDS; buffer buf^1 is free
     const int kv0 = j * BC;
     const int jn = next_kept(j + 1);
-    if (jn < ntiles) load_tile(jn);  // in flight while this tile is computed
+    if (jn < ntiles) stage(jn, buf ^ 1);   // in flight while this tile is computed
+    const unsigned char* sK = smem + buf * 2 * TB;
+    const unsigned char* sV = sK + TB;
 
     // ---- S^T = K_j Q^T -------------------------------------------------
     f32x16 s[NH];
@@ -155,7 +116,7 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
       s[h] = f32x16{};
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const frag a = E::load(sK + (32 * h + l32) * LDK + 16 * t + 8 * g);
+        const frag a = row_frag<T, D>(sK, 32 * h + l32, t, g);
         s[h] = E::mma(a, qf[t], s[h]);
       }
     }
@@ -174,8 +135,8 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     }
 
     // ---- online softmax ----------------------------------------------------
-    // c > 0 (the host clamps it to at least FLT_MIN), so a masked score gives
-    // 2^(-inf) = 0 and the row max of kept scores times c is the max of S*c.
+    // c > 0, so a masked score gives 2^(-inf) = 0 and c times the row max of
+    // the kept scores is the max of S*c.
     float mx = neg_inf();
 #pragma unroll
     for (int h = 0; h < NH; ++h)
@@ -213,9 +174,10 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     for (int b = 0; b < ND; ++b)
 #pragma unroll
       for (int cc = 0; cc < 2 * NH; ++cc) {
-        const frag a = E::load(sVt + (32 * b + l32) * LDV + 16 * cc + 8 * g);
+        const frag a = trans_frag<T, D>(sV, b, cc, lane);
         oacc[b] = E::mma(a, pf[cc >> 1][cc & 1], oacc[b]);
       }
+    buf ^= 1;
     j = jn;
   }
 
