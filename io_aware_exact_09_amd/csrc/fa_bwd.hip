@@ -167,11 +167,20 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
     const bool need_mask = CAUSAL && (q0 < kw + 31);
 #pragma unroll
     for (int qh = 0; qh < NQH; ++qh) {
+      // Operands are read into registers a batch ahead of their MFMAs so the
+      // LDS latency overlaps the matrix work.
+      frag aq[NT], ao[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        aq[t] = row_frag<T, D>(sQ, 32 * qh + l32, t, g);
+        ao[t] = row_frag<T, D>(sdO, 32 * qh + l32, t, g);
+      }
+      sched_fence();
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        s = E::mma(row_frag<T, D>(sQ, 32 * qh + l32, t, g), kf[t], s);
-        dp = E::mma(row_frag<T, D>(sdO, 32 * qh + l32, t, g), vf[t], dp);
+        s = E::mma(aq[t], kf[t], s);
+        dp = E::mma(ao[t], vf[t], dp);
       }
       // Register r holds query 32qh + 8(r/4) + 4g + r%4 of this tile.
 #pragma unroll
@@ -193,10 +202,17 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
         const frag pf = E::from_c(s, t);
         const frag df = E::from_c(dp, t);
         const int cc = 2 * qh + t;      // 16-row chunk of the query tile
+        frag ot[ND], qt[ND];
 #pragma unroll
         for (int b = 0; b < ND; ++b) {
-          dvacc[b] = E::mma(trans_frag<T, D>(sdO, b, cc, lane), pf, dvacc[b]);
-          dkacc[b] = E::mma(trans_frag<T, D>(sQ, b, cc, lane), df, dkacc[b]);
+          ot[b] = trans_frag<T, D>(sdO, b, cc, lane);
+          qt[b] = trans_frag<T, D>(sQ, b, cc, lane);
+        }
+        sched_fence();
+#pragma unroll
+        for (int b = 0; b < ND; ++b) {
+          dvacc[b] = E::mma(ot[b], pf, dvacc[b]);
+          dkacc[b] = E::mma(qt[b], df, dkacc[b]);
         }
       }
     }
@@ -314,11 +330,18 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
     const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > q0 + 32 * w);
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
+      frag ak[NT], av[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        ak[t] = row_frag<T, D>(sK, 32 * h + l32, t, g);
+        av[t] = row_frag<T, D>(sV, 32 * h + l32, t, g);
+      }
+      sched_fence();
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        s = E::mma(row_frag<T, D>(sK, 32 * h + l32, t, g), qf[t], s);
-        dp = E::mma(row_frag<T, D>(sV, 32 * h + l32, t, g), of[t], dp);
+        s = E::mma(ak[t], qf[t], s);
+        dp = E::mma(av[t], of[t], dp);
       }
       // Register r holds key kv0 + 4g + 32h + 8(r/4) + r%4.
       const int lim = (CAUSAL ? min(N, qrow + 1) : N) - kv0 - 4 * g - 32 * h;
@@ -332,9 +355,12 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
       for (int t = 0; t < 2; ++t) {
         const frag df = E::from_c(dp, t);
         const int cc = 2 * h + t;
+        frag kt[ND];
 #pragma unroll
-        for (int b = 0; b < ND; ++b)
-          dqacc[b] = E::mma(trans_frag<T, D>(sK, b, cc, lane), df, dqacc[b]);
+        for (int b = 0; b < ND; ++b) kt[b] = trans_frag<T, D>(sK, b, cc, lane);
+        sched_fence();
+#pragma unroll
+        for (int b = 0; b < ND; ++b) dqacc[b] = E::mma(kt[b], df, dqacc[b]);
       }
     }
     buf ^= 1;

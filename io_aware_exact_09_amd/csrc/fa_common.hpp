@@ -141,6 +141,11 @@ __device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
 // fragments loaded before the loop) are complete.
 __device__ __forceinline__ void wait_global_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Keeps the compiler's scheduler from moving instructions across this point
+// (used to issue a batch of LDS operand reads before the MFMAs that consume
+// them, so their latency overlaps the matrix work).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 // One operand fragment (8 contraction values) read straight from global memory.
 template <typename T>
 __device__ __forceinline__ typename Elem<T>::frag gload_frag(rsrc_t r, uint32_t off) {

@@ -110,15 +110,18 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     const unsigned char* sV = sK + TB;
 
     // ---- S^T = K_j Q^T -------------------------------------------------
+    // Operands are read into registers a batch ahead of their MFMAs so the
+    // LDS latency overlaps the matrix work.
     f32x16 s[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
+      frag ak[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) ak[t] = row_frag<T, D>(sK, 32 * h + l32, t, g);
+      sched_fence();
       s[h] = f32x16{};
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const frag a = row_frag<T, D>(sK, 32 * h + l32, t, g);
-        s[h] = E::mma(a, qf[t], s[h]);
-      }
+      for (int t = 0; t < NT; ++t) s[h] = E::mma(ak[t], qf[t], s[h]);
     }
 
     // ---- mask (diagonal / tail tiles only) -------------------------------
@@ -171,12 +174,14 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
       pf[h][1] = E::from_c(s[h], 1);
     }
 #pragma unroll
-    for (int b = 0; b < ND; ++b)
+    for (int b = 0; b < ND; ++b) {
+      frag av[2 * NH];
 #pragma unroll
-      for (int cc = 0; cc < 2 * NH; ++cc) {
-        const frag a = trans_frag<T, D>(sV, b, cc, lane);
-        oacc[b] = E::mma(a, pf[cc >> 1][cc & 1], oacc[b]);
-      }
+      for (int cc = 0; cc < 2 * NH; ++cc) av[cc] = trans_frag<T, D>(sV, b, cc, lane);
+      sched_fence();
+#pragma unroll
+      for (int cc = 0; cc < 2 * NH; ++cc) oacc[b] = E::mma(av[cc], pf[cc >> 1][cc & 1], oacc[b]);
+    }
     buf ^= 1;
     j = jn;
   }
