@@ -253,7 +253,7 @@ struct DqCfg {
 
 template <typename T, int D, bool CAUSAL, bool MASKED>
 __global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
+__attribute__((amdgpu_waves_per_eu(Occupancy<T, D>::dq, Occupancy<T, D>::dq)))
 fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                  const T* __restrict__ dO, const float* __restrict__ LSE,
                  const float* __restrict__ delta, T* __restrict__ dQ,
@@ -330,18 +330,23 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
     const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > q0 + 32 * w);
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
-      frag ak[NT], av[NT];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        ak[t] = row_frag<T, D>(sK, 32 * h + l32, t, g);
-        av[t] = row_frag<T, D>(sV, 32 * h + l32, t, g);
-      }
-      sched_fence();
+      // Operands in sub-batches of SB chunks (register budget of two waves
+      // per SIMD); the other wave on the SIMD covers the LDS latency.
+      constexpr int SB = NT >= 8 ? 4 : NT;
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        s = E::mma(ak[t], qf[t], s);
-        dp = E::mma(av[t], of[t], dp);
+      for (int t0 = 0; t0 < NT; t0 += SB) {
+        frag ak[SB], av[SB];
+#pragma unroll
+        for (int t = 0; t < SB; ++t) {
+          ak[t] = row_frag<T, D>(sK, 32 * h + l32, t0 + t, g);
+          av[t] = row_frag<T, D>(sV, 32 * h + l32, t0 + t, g);
+        }
+#pragma unroll
+        for (int t = 0; t < SB; ++t) {
+          s = E::mma(ak[t], qf[t0 + t], s);
+          dp = E::mma(av[t], of[t0 + t], dp);
+        }
       }
       // Register r holds key kv0 + 4g + 32h + 8(r/4) + r%4.
       const int lim = (CAUSAL ? min(N, qrow + 1) : N) - kv0 - 4 * g - 32 * h;
@@ -358,7 +363,6 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
         frag kt[ND];
 #pragma unroll
         for (int b = 0; b < ND; ++b) kt[b] = trans_frag<T, D>(sK, b, cc, lane);
-        sched_fence();
 #pragma unroll
         for (int b = 0; b < ND; ++b) dqacc[b] = E::mma(kt[b], df, dqacc[b]);
       }

@@ -37,6 +37,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaskBlock = 128;
 constexpr int kThreads = 256;   // 4 waves per work-group
+// The forward moves its reference max only when a row max grows by more than
+// this many doublings (see fa_fwd.hip); probabilities stay <= 2^kLazy.
+constexpr float kLazy = 8.0f;
 
 // Exponent coefficient c = scale * log2(e), clamped to at least FLT_MIN so
 // that c > 0: a masked score (-inf) then always gives 2^(-inf * c) = 0.  For
@@ -274,6 +277,15 @@ __device__ __forceinline__ typename Elem<T>::frag trans_frag(const unsigned char
   }
   return f;
 }
+
+// Waves per SIMD each kernel is compiled for (two waves let one wave's
+// softmax arithmetic overlap the other's matrix work; the fp32 path at
+// d = 128 needs the full register file of one wave).
+template <typename T, int D>
+struct Occupancy {
+  static constexpr int fwd = (sizeof(T) == 2 || D == 64) ? 2 : 1;
+  static constexpr int dq = (sizeof(T) == 2 || D == 64) ? 2 : 1;
+};
 
 // ---------------------------------------------------------------------------
 // Work-group -> (head, block) mapping.

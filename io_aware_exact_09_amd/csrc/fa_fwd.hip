@@ -39,7 +39,7 @@ struct FwdCfg {
 
 template <typename T, int D, bool CAUSAL, bool MASKED>
 __global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(2, 2)))
+__attribute__((amdgpu_waves_per_eu(Occupancy<T, D>::fwd, Occupancy<T, D>::fwd)))
 fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
               T* __restrict__ O, float* __restrict__ LSE, const uint8_t* __restrict__ mask,
               int BH, int N, int T_tiles, float c /* scale*log2e, > 0 */) {
@@ -139,7 +139,10 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
 
     // ---- online softmax ----------------------------------------------------
     // c > 0, so a masked score gives 2^(-inf) = 0 and c times the row max of
-    // the kept scores is the max of S*c.
+    // the kept scores is the max of S*c.  The reference m_run moves only when
+    // a row's tile max exceeds it by more than kLazy (log2 units): P stays
+    // <= 2^kLazy, numerator and denominator share the same reference, and the
+    // O/l rescale (one multiply per accumulator) is skipped on most tiles.
     float mx = neg_inf();
 #pragma unroll
     for (int h = 0; h < NH; ++h)
@@ -147,24 +150,28 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[h][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_tile = mx * c;
-    const float m_new = fmaxf(m_run, m_tile);
-    const float m_use = m_new == neg_inf() ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);   // 0 while m_run = -inf
-    float psum = 0.f;
+    const bool grow = m_tile > m_run + kLazy;          // always true on the first kept tile
+    if (__any(grow)) {
+      const float m_new = grow ? m_tile : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run = -inf
+#pragma unroll
+      for (int b = 0; b < ND; ++b) oacc[b] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == neg_inf() ? 0.f : m_run;
+    // Row sum in fp32 from the unrounded probabilities (the log-sum-exp the
+    // backward relies on must not carry the bf16 rounding of P).
+    float psum[NH][4] = {};
 #pragma unroll
     for (int h = 0; h < NH; ++h)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[h][r], c, -m_use));
-        s[h][r] = p;
-        psum += p;
+        s[h][r] = __builtin_amdgcn_exp2f(fmaf(s[h][r], c, -m_use));
+        psum[h][r & 3] += s[h][r];
       }
-    l_run = fmaf(l_run, alpha, psum);
-    if (__any(alpha != 1.0f)) {
 #pragma unroll
-      for (int b = 0; b < ND; ++b) oacc[b] *= alpha;
-    }
-    m_run = m_new;
+    for (int h = 0; h < NH; ++h) l_run += (psum[h][0] + psum[h][1]) + (psum[h][2] + psum[h][3]);
 
     // ---- O^T += V_j^T P^T ----------------------------------------------------
     frag pf[NH][2];
