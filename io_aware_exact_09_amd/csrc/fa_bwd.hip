@@ -146,78 +146,206 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   f32x16 dkacc[ND], dvacc[ND];
 #pragma unroll
   for (int b = 0; b < ND; ++b) { dkacc[b] = f32x16{}; dvacc[b] = f32x16{}; }
+  LaneOffsets<T, D> lo;
+  lo.init(lane);
 
-  int i = next_kept(first);
-  int buf = 0;
-  if (i < ntiles) stage(i, 0);
-  while (i < ntiles) {
-    wait_global_loads();
-    if (tid < BQ) {
-      // Rows past N, and rows that keep no key (LSE = -inf), get P = 0.
-      sL[buf][tid] = (lrow_pre < N && lpre != neg_inf()) ? lpre * kLog2e : pos_inf();
-      sD[buf][tid] = dpre;
-    }
-    __syncthreads();
-    const int q0 = i * BQ;
-    const int in = next_kept(i + 1);
-    if (in < ntiles) stage(in, buf ^ 1);
-    const unsigned char* sQ = smem + buf * 2 * TB;
+  // One tile iteration.  MASKED_TILE (the tile crosses this wave's causal
+  // diagonal) is compile-time, so unmasked tiles carry no mask arithmetic.
+  auto tile = [&](auto mask_tag, auto buf_sel, int q0) {
+    const int BUF = buf_sel;
+    constexpr bool MASKED_TILE = decltype(mask_tag)::value;
+    const unsigned char* sQ = smem + BUF * 2 * TB;
     const unsigned char* sdO = sQ + TB;
+      // The tile is processed as a pipeline of MFMA blocks:
+      //   S/dP of query half 0 (NT/SB blocks of 2*SB MFMAs), S/dP of half 1,
+      //   dV/dK of half 0 (2 blocks of 2*ND MFMAs), dV/dK of half 1.
+      // Each block's LDS operands are read while the previous block's MFMAs run,
+      // and the P/dS arithmetic of a half is spread over the blocks that follow
+      // it, between their MFMAs.
+      constexpr int SB = NT >= 8 ? 4 : NT;          // d-chunks per S/dP block
+      constexpr int NSB = NT / SB;                  // S/dP blocks per half
 
-    const bool need_mask = CAUSAL && (q0 < kw + 31);
+      // S/dP block (half qh, d-chunks t0 .. t0+SB-1)
+      auto sdp_read = [&](int qh, int t0, frag* aq, frag* ao) {
 #pragma unroll
-    for (int qh = 0; qh < NQH; ++qh) {
-      // Operands are read into registers a batch ahead of their MFMAs so the
-      // LDS latency overlaps the matrix work.
-      frag aq[NT], ao[NT];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        aq[t] = row_frag<T, D>(sQ, 32 * qh + l32, t, g);
-        ao[t] = row_frag<T, D>(sdO, 32 * qh + l32, t, g);
-      }
-      sched_fence();
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        s = E::mma(aq[t], kf[t], s);
-        dp = E::mma(ao[t], vf[t], dp);
-      }
-      // Register r holds query 32qh + 8(r/4) + 4g + r%4 of this tile.
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int qi = 32 * qh + 8 * a + 4 * g;
-        const f32x4 lv = *reinterpret_cast<const f32x4*>(&sL[buf][qi]);
-        const f32x4 dv = *reinterpret_cast<const f32x4*>(&sD[buf][qi]);
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int r = 4 * a + x;
-          float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[x]));
-          if (need_mask && krow > q0 + qi + x) p = 0.f;
-          s[r] = p;
-          dp[r] = p * (dp[r] - dv[x]);
+        for (int t = 0; t < SB; ++t) {
+          if constexpr (sizeof(T) == 2) {
+            const unsigned char* p = sQ + lo.row[t0 + t] + 32 * qh * RB;
+            aq[t] = row_frag_at<T>(p);
+            ao[t] = row_frag_at<T>(p + TB);
+          } else {
+            aq[t] = row_frag<T, D>(sQ, 32 * qh + l32, t0 + t, g);
+            ao[t] = row_frag<T, D>(sdO, 32 * qh + l32, t0 + t, g);
+          }
         }
-      }
+      };
+      auto sdp_mma = [&](int t0, const frag* aq, const frag* ao, f32x16& sv, f32x16& dpv) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const frag pf = E::from_c(s, t);
-        const frag df = E::from_c(dp, t);
-        const int cc = 2 * qh + t;      // 16-row chunk of the query tile
-        frag ot[ND], qt[ND];
+        for (int t = 0; t < SB; ++t) {
+          sv = E::mma(aq[t], kf[t0 + t], sv);
+          dpv = E::mma(ao[t], vf[t0 + t], dpv);
+        }
+      };
+      // P = 2^(S c - LSE log2 e), dS = P (dP - D) for register groups
+      // a0 .. a1-1 (register r holds query 32qh + 8(r/4) + 4g + r%4).
+      auto pds_part = [&](int qh, int a0, int a1, f32x16& sv, f32x16& dpv) {
+#pragma unroll
+        for (int a = a0; a < a1; ++a) {
+          const int qi = 32 * qh + 8 * a + 4 * g;
+          const f32x4 lv = *reinterpret_cast<const f32x4*>(&sL[BUF][qi]);
+          const f32x4 dv = *reinterpret_cast<const f32x4*>(&sD[BUF][qi]);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const int r = 4 * a + x;
+            float p = __builtin_amdgcn_exp2f(fmaf(sv[r], c, -lv[x]));
+            if (MASKED_TILE && krow > q0 + qi + x) p = 0.f;
+            sv[r] = p;
+            dpv[r] = p * (dpv[r] - dv[x]);
+          }
+        }
+      };
+      auto pds_pack = [&](const f32x16& sv, const f32x16& dpv, frag* pf, frag* df) {
+        pf[0] = E::from_c(sv, 0);
+        pf[1] = E::from_c(sv, 1);
+        df[0] = E::from_c(dpv, 0);
+        df[1] = E::from_c(dpv, 1);
+      };
+      // dV/dK block (half qh, 16-row chunk t of the half)
+      auto dvdk_read = [&](int qh, int t, frag* ot, frag* qt) {
 #pragma unroll
         for (int b = 0; b < ND; ++b) {
-          ot[b] = trans_frag<T, D>(sdO, b, cc, lane);
-          qt[b] = trans_frag<T, D>(sQ, b, cc, lane);
+          if constexpr (sizeof(T) == 2) {
+            const unsigned char* p0 = sQ + lo.tr[b][0] + 16 * (2 * qh + t) * RB;
+            const unsigned char* p1 = sQ + lo.tr[b][1] + 16 * (2 * qh + t) * RB;
+            ot[b] = trans_frag_at(p0 + TB, p1 + TB);
+            qt[b] = trans_frag_at(p0, p1);
+          } else {
+            ot[b] = trans_frag<T, D>(sdO, b, 2 * qh + t, lane);
+            qt[b] = trans_frag<T, D>(sQ, b, 2 * qh + t, lane);
+          }
         }
-        sched_fence();
+      };
+      auto dvdk_mma = [&](const frag* ot, const frag* qt, const frag& pf, const frag& df) {
 #pragma unroll
         for (int b = 0; b < ND; ++b) {
           dvacc[b] = E::mma(ot[b], pf, dvacc[b]);
           dkacc[b] = E::mma(qt[b], df, dkacc[b]);
         }
+      };
+
+      f32x16 s0 = f32x16{}, dp0 = f32x16{};
+      frag pf0[2], df0[2];
+      frag xa[SB], xb[SB];        // operand set of the block being issued
+      frag ya[SB], yb[SB];        // operand set prefetched for the next block
+      if constexpr (NQH == 2) {
+        f32x16 s1 = f32x16{}, dp1 = f32x16{};
+        frag pf1[2], df1[2];
+        frag ta[ND], tb[ND], ua[ND], ub[ND];
+        sdp_read(0, 0, xa, xb);
+        sched_fence();
+        // S/dP, half 0
+#pragma unroll
+        for (int k = 0; k < NSB; ++k) {
+          if (k + 1 < NSB) sdp_read(0, (k + 1) * SB, ya, yb);
+          else sdp_read(1, 0, ya, yb);
+          sdp_mma(k * SB, xa, xb, s0, dp0);
+          interleave<2 * SB, 2 * SB, 0>();
+          sched_fence();
+#pragma unroll
+          for (int t = 0; t < SB; ++t) { xa[t] = ya[t]; xb[t] = yb[t]; }
+        }
+        // S/dP, half 1, with P/dS of half 0 in between
+#pragma unroll
+        for (int k = 0; k < NSB; ++k) {
+          if (k + 1 < NSB) sdp_read(1, (k + 1) * SB, ya, yb);
+          else dvdk_read(0, 0, ta, tb);
+          sdp_mma(k * SB, xa, xb, s1, dp1);
+          pds_part(0, k * 4 / NSB, (k + 1) * 4 / NSB, s0, dp0);
+          if (k + 1 == NSB) pds_pack(s0, dp0, pf0, df0);
+          if (k + 1 < NSB) interleave<2 * SB, 2 * SB + 8 / NSB, 5>();
+          else interleave<2 * SB, 4 * ND + 8 / NSB, 5>();
+          sched_fence();
+#pragma unroll
+          for (int t = 0; t < SB; ++t) { xa[t] = ya[t]; xb[t] = yb[t]; }
+        }
+        // dV/dK, half 0, with P/dS of half 1 in between
+        dvdk_read(0, 1, ua, ub);
+        dvdk_mma(ta, tb, pf0[0], df0[0]);
+        pds_part(1, 0, 2, s1, dp1);
+        interleave<2 * ND, 4 * ND + 4, 6>();
+        sched_fence();
+        dvdk_read(1, 0, ta, tb);
+        dvdk_mma(ua, ub, pf0[1], df0[1]);
+        pds_part(1, 2, 4, s1, dp1);
+        pds_pack(s1, dp1, pf1, df1);
+        interleave<2 * ND, 4 * ND + 4, 6>();
+        sched_fence();
+        // dV/dK, half 1
+        dvdk_read(1, 1, ua, ub);
+        dvdk_mma(ta, tb, pf1[0], df1[0]);
+        interleave<2 * ND, 4 * ND, 0>();
+        sched_fence();
+        dvdk_mma(ua, ub, pf1[1], df1[1]);
+      } else {
+        frag ta[ND], tb[ND];
+#pragma unroll
+        for (int k = 0; k < NSB; ++k) {
+          sdp_read(0, k * SB, xa, xb);
+          sdp_mma(k * SB, xa, xb, s0, dp0);
+        }
+        pds_part(0, 0, 4, s0, dp0);
+        pds_pack(s0, dp0, pf0, df0);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          dvdk_read(0, t, ta, tb);
+          dvdk_mma(ta, tb, pf0[t], df0[t]);
+        }
       }
+  };
+  // Wait for tile i (buffer BUF), publish its row statistics, prefetch the
+  // next kept tile into the other buffer, then run the tile.
+  auto step = [&](auto buf_sel, int i, int in) {
+    const int BUF = buf_sel;
+    wait_global_loads();
+    if (tid < BQ) {
+      // Rows past N, and rows that keep no key (LSE = -inf), get P = 0.
+      sL[BUF][tid] = (lrow_pre < N && lpre != neg_inf()) ? lpre * kLog2e : pos_inf();
+      sD[BUF][tid] = dpre;
     }
-    buf ^= 1;
-    i = in;
+    __syncthreads();
+    const int q0 = i * BQ;
+    if (in < ntiles) stage(in, BUF ^ 1);
+    if constexpr (sizeof(T) == 4) {
+      tile(BoolTag<CAUSAL>{}, buf_sel, q0);   // one body: the fp32 path needs every register
+    } else {
+      if (CAUSAL && q0 < kw + 31) tile(BoolTag<true>{}, buf_sel, q0);
+      else tile(BoolTag<false>{}, buf_sel, q0);
+    }
+  };
+
+  int i = next_kept(first);
+  if (i < ntiles) stage(i, 0);
+  if constexpr (CAUSAL && sizeof(T) == 2) {
+    // Two iterations per trip with the buffer index a compile-time constant,
+    // so the LDS offsets are immediates.  (The register allocator handles
+    // this shape well only for the causal instances.)
+    while (i < ntiles) {
+      int in = next_kept(i + 1);
+      step(IntTag<0>{}, i, in);
+      i = in;
+      if (i >= ntiles) break;
+      in = next_kept(i + 1);
+      step(IntTag<1>{}, i, in);
+      i = in;
+    }
+  } else {
+    int buf = 0;
+    while (i < ntiles) {
+      const int in = next_kept(i + 1);
+      step(buf, i, in);
+      buf ^= 1;
+      i = in;
+    }
   }
 
   // dV^T / dK^T C layout: lane (key l32, g), register r -> d = 32b + 8(r/4) + 4g + r%4.

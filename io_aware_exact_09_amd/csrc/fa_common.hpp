@@ -53,6 +53,13 @@ inline float score_coef(float scale) {
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 __device__ __forceinline__ float pos_inf() { return __builtin_inff(); }
 
+// Compile-time tags for generic lambdas.
+template <int V> struct IntTag {
+  static constexpr int value = V;
+  __device__ constexpr operator int() const { return V; }
+};
+template <bool V> struct BoolTag { static constexpr bool value = V; };
+
 // Position of contraction index x inside its 16-group in a transposed tile.
 __device__ __forceinline__ constexpr int perm16(int x) {
   return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
@@ -149,6 +156,20 @@ __device__ __forceinline__ void wait_global_loads() { __builtin_amdgcn_s_waitcnt
 // them, so their latency overlaps the matrix work).
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// Scheduling hint for one straight-line region: issue the region's first
+// `READS` LDS reads, then alternate one MFMA with up to `VPM` VALU
+// instructions, `MFMAS` times.  Instructions the pattern does not claim are
+// placed freely by the scheduler; dependencies always win.
+template <int MFMAS, int READS, int VPM>
+__device__ __forceinline__ void interleave() {
+  __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);   // DS read
+#pragma unroll
+  for (int i = 0; i < MFMAS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);   // VALU
+  }
+}
+
 // One operand fragment (8 contraction values) read straight from global memory.
 template <typename T>
 __device__ __forceinline__ typename Elem<T>::frag gload_frag(rsrc_t r, uint32_t off) {
@@ -237,6 +258,45 @@ __device__ __forceinline__ typename Elem<T>::frag row_frag(const unsigned char* 
   return f;
 }
 
+// Precomputed per-lane LDS offsets for the operand reads of one kernel.  The
+// swizzle depends only on (row mod 16), so for a lane the offsets of the
+// natural reads differ only per d-chunk t, and those of the transposed reads
+// only per (output block b, row group h); row-block, 16-row chunk and
+// tensor offsets are compile-time and go into the instruction's immediate.
+template <typename T, int D>
+struct LaneOffsets {
+  static constexpr int NT = D / 16, ND = D / 32;
+  uint32_t row[NT];        // row l32, chunk 2t + g (bf16)
+  uint32_t tr[ND][2];      // transposed reads: rows rl + 8h, columns of block b
+
+  __device__ void init(int lane) {
+    using L = Tile<T, D>;
+    const int l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) row[t] = L::off(l32, 2 * t + g);
+    if constexpr (sizeof(T) == 2) {
+      const int q = lane >> 4, j = lane & 15;
+      const int rl = 4 * (q >> 1) + (j >> 2);
+#pragma unroll
+      for (int b = 0; b < ND; ++b) {
+        const int col = 32 * b + 16 * (q & 1) + 4 * (j & 3);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) tr[b][h] = L::off(rl + 8 * h, col >> 3) + ((col & 7) << 1);
+      }
+    }
+  }
+};
+
+// Natural-order bf16 operand at a precomputed lane offset (see row_frag).
+// (fp32 operands span two swizzled chunks and use row_frag.)
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::frag row_frag_at(const unsigned char* p) {
+  static_assert(sizeof(T) == 2, "bf16 only");
+  typename Elem<T>::frag f;
+  f.v = *reinterpret_cast<const bf16x8*>(p);
+  return f;
+}
+
 // C-shaped transposed operand: the A operand of a contraction over the tile's
 // rows, for output rows 32 b .. 32 b + 31 (= tile columns) and contraction
 // rows 16 cc .. 16 cc + 15.  Lane (l32, g) gets, for item e, the element at
@@ -275,6 +335,21 @@ __device__ __forceinline__ typename Elem<T>::frag trans_frag(const unsigned char
       f.hi[e] = *reinterpret_cast<const float*>(tile + L::off(r0 + 8, col >> 2) + ((col & 3) << 2));
     }
   }
+  return f;
+}
+
+// Transposed operand (bf16) at precomputed offsets: p0/p1 address the two
+// 4-row groups (see trans_frag).
+__device__ __forceinline__ Elem<__bf16>::frag trans_frag_at(const unsigned char* p0,
+                                                            const unsigned char* p1) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)as_lds(const_cast<unsigned char*>(p0)));
+  const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)as_lds(const_cast<unsigned char*>(p1)));
+  Elem<__bf16>::frag f;
+  f.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
   return f;
 }
 
