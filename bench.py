@@ -52,7 +52,26 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the CPU oracle sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one plain device copy of FA_COPY_PROBE_BYTES (512 MiB) first, "
+                         "to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+def recorded_traffic(workload, kernel):
+    """Calibrated HBM bytes per launch of `kernel` from profiles/, if they
+    were measured on the current kernel sources (else None)."""
+    from io_aware_exact_09_amd import profiles
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_hash") != profiles.source_hash() or kernel not in rec:
+        return None
+    k = rec[kernel]
+    if "read_bytes" not in k or "write_bytes" not in k:
+        return None
+    return k["read_bytes"] + k["write_bytes"]
 
 
 def cpu_baseline(w, x, budget_s):
@@ -115,6 +134,13 @@ def main():
     ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8,
                      device=dev)
     sc, cz = w.scale, w.causal
+    if args.copy_probe:
+        n = int(os.environ.get("FA_COPY_PROBE_BYTES", 512 << 20))
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)            # reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        del src, dst
 
     phases = ["fwd", "pre", "dkdv", "dq"]
 
@@ -160,11 +186,13 @@ def main():
     if dom == "pre":
         ach = hb["pre_kernel"] / (avg[dom] * 1e-3) / 1e9
         roof = {"kernel": names[dom], "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None}
+                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                "traffic": recorded_traffic(w.name, names[dom])}
     else:
         ach = kflops[dom] / (avg[dom] * 1e-3) / 1e12
         roof = {"kernel": names[dom], "bound": "mfma", "achieved": ach, "peak": peak,
-                "unit": "TFLOP/s", "frac": ach / peak, "traffic": None,
+                "unit": "TFLOP/s", "frac": ach / peak,
+                "traffic": recorded_traffic(w.name, names[dom]),
                 "algorithmic_flops_per_launch": kflops[dom], "avg_launch_ms": avg[dom]}
 
     kernels = {}

@@ -441,21 +441,24 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
 #pragma unroll
   for (int b = 0; b < ND; ++b) dqacc[b] = f32x16{};
 
+  // Precomputed operand offsets when the register budget of two waves per
+  // SIMD allows it (bf16, d = 64); otherwise addresses are formed per read.
+  constexpr bool USE_LO = sizeof(T) == 2 && D == 64;
+  LaneOffsets<T, D> lo;
+  if constexpr (USE_LO) lo.init(lane);
   int j = next_kept(0);
-  int buf = 0;
   if (j < ntiles) stage(j, 0);
   wait_global_loads();
   const float lse2 = (qrow < N && lrow != neg_inf()) ? lrow * kLog2e : pos_inf();
-  while (j < ntiles) {
-    wait_global_loads();
-    __syncthreads();
-    const int kv0 = j * BC;
-    const int jn = next_kept(j + 1);
-    if (jn < ntiles) stage(jn, buf ^ 1);
-    const unsigned char* sK = smem + buf * 2 * TB;
-    const unsigned char* sV = sK + TB;
 
-    const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > q0 + 32 * w);
+  // One key tile.  MASKED_TILE: the tile crosses this wave's causal diagonal
+  // or the end of the sequence (a compile-time tag where a second body fits
+  // the register budget, so other tiles carry no mask arithmetic).
+  auto tile = [&](auto mask_sel, auto buf_sel, int kv0) {
+    const bool MASKED_TILE = mask_sel;
+    const int BUF = buf_sel;
+    const unsigned char* sK = smem + BUF * 2 * TB;
+    const unsigned char* sV = sK + TB;
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       // Operands in sub-batches of SB chunks (register budget of two waves
@@ -467,8 +470,14 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
         frag ak[SB], av[SB];
 #pragma unroll
         for (int t = 0; t < SB; ++t) {
-          ak[t] = row_frag<T, D>(sK, 32 * h + l32, t0 + t, g);
-          av[t] = row_frag<T, D>(sV, 32 * h + l32, t0 + t, g);
+          if constexpr (USE_LO) {
+            const unsigned char* p = sK + lo.row[t0 + t] + 32 * h * RB;
+            ak[t] = row_frag_at<T>(p);
+            av[t] = row_frag_at<T>(p + TB);
+          } else {
+            ak[t] = row_frag<T, D>(sK, 32 * h + l32, t0 + t, g);
+            av[t] = row_frag<T, D>(sV, 32 * h + l32, t0 + t, g);
+          }
         }
 #pragma unroll
         for (int t = 0; t < SB; ++t) {
@@ -481,7 +490,7 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
-        if (need_mask && 8 * (r >> 2) + (r & 3) >= lim) p = 0.f;
+        if (MASKED_TILE && 8 * (r >> 2) + (r & 3) >= lim) p = 0.f;
         dp[r] = p * (dp[r] - dval);
       }
 #pragma unroll
@@ -490,13 +499,50 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
         const int cc = 2 * h + t;
         frag kt[ND];
 #pragma unroll
-        for (int b = 0; b < ND; ++b) kt[b] = trans_frag<T, D>(sK, b, cc, lane);
+        for (int b = 0; b < ND; ++b) {
+          if constexpr (USE_LO)
+            kt[b] = trans_frag_at(sK + lo.tr[b][0] + 16 * cc * RB, sK + lo.tr[b][1] + 16 * cc * RB);
+          else
+            kt[b] = trans_frag<T, D>(sK, b, cc, lane);
+        }
 #pragma unroll
         for (int b = 0; b < ND; ++b) dqacc[b] = E::mma(kt[b], df, dqacc[b]);
       }
     }
-    buf ^= 1;
-    j = jn;
+  };
+  auto step = [&](auto buf_sel, int j, int jn) {
+    const int BUF = buf_sel;
+    wait_global_loads();
+    __syncthreads();
+    const int kv0 = j * BC;
+    if (jn < ntiles) stage(jn, BUF ^ 1);
+    const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > q0 + 32 * w);
+    if constexpr (sizeof(T) == 2 && D == 64) {
+      // Separate masked / unmasked bodies where the registers allow it.
+      if (need_mask) tile(BoolTag<true>{}, buf_sel, kv0);
+      else tile(BoolTag<false>{}, buf_sel, kv0);
+    } else {
+      tile(need_mask, buf_sel, kv0);
+    }
+  };
+  if constexpr (CAUSAL && sizeof(T) == 2 && D == 64) {
+    while (j < ntiles) {   // two tiles per trip, buffer index compile-time
+      int jn = next_kept(j + 1);
+      step(IntTag<0>{}, j, jn);
+      j = jn;
+      if (j >= ntiles) break;
+      jn = next_kept(j + 1);
+      step(IntTag<1>{}, j, jn);
+      j = jn;
+    }
+  } else {
+    int buf = 0;
+    while (j < ntiles) {
+      const int jn = next_kept(j + 1);
+      step(buf, j, jn);
+      buf ^= 1;
+      j = jn;
+    }
   }
 
   if (qrow < N) {

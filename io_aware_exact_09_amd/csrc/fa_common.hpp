@@ -58,7 +58,10 @@ template <int V> struct IntTag {
   static constexpr int value = V;
   __device__ constexpr operator int() const { return V; }
 };
-template <bool V> struct BoolTag { static constexpr bool value = V; };
+template <bool V> struct BoolTag {
+  static constexpr bool value = V;
+  __device__ constexpr operator bool() const { return V; }
+};
 
 // Position of contraction index x inside its 16-group in a transposed tile.
 __device__ __forceinline__ constexpr int perm16(int x) {

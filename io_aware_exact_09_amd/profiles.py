@@ -1,0 +1,117 @@
+"""Turn rocprofv3 output into the short text summaries kept under profiles/.
+
+    python -m io_aware_exact_09_amd.profiles stats <kernel_stats.csv> <out.md> "<command>"
+    python -m io_aware_exact_09_amd.profiles traffic <fetch_dir> <write_dir> <workload> \
+        <out.json> "<fetch command>" "<write command>"
+
+``stats`` condenses a ``--kernel-trace --stats`` run (per-kernel calls and
+average duration).  ``traffic`` reads two ``--pmc FETCH_SIZE`` /
+``--pmc WRITE_SIZE`` runs of ``bench.py --copy-probe``: the probe is a plain
+device-to-device copy of a known number of bytes, and the ratio of those bytes
+to what the counter reports for it calibrates the counter for the attention
+kernels of the same run.  The JSON records, per attention kernel, the
+calibrated HBM bytes per launch and a hash of the kernel sources, so that
+bench.py reports the traffic only while the kernels are unchanged.
+"""
+
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+PROFILES = os.path.join(ROOT, "profiles")
+
+KERNELS = ("fa_fwd_kernel", "fa_bwd_delta_kernel", "fa_bwd_dkdv_kernel", "fa_bwd_dq_kernel")
+
+
+def source_hash() -> str:
+    """Hash of the HIP sources the kernels are built from."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(kernel_name: str) -> str:
+    for k in KERNELS:
+        if k in kernel_name:
+            return k
+    if "copy" in kernel_name.lower() or "elementwise" in kernel_name:
+        return "copy:" + kernel_name[:60]
+    return kernel_name[:60]
+
+
+def _rows(path_or_dir: str, suffix: str):
+    paths = [path_or_dir] if path_or_dir.endswith(".csv") else \
+        glob.glob(os.path.join(path_or_dir, "**", f"*{suffix}"), recursive=True)
+    for p in paths:
+        with open(p) as f:
+            yield from csv.DictReader(f)
+
+
+def stats_summary(stats_csv: str, command: str) -> str:
+    lines = ["# rocprofv3 kernel-trace summary", "", f"Command: `{command}`", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in _rows(stats_csv, "kernel_stats.csv"):
+        lines.append("| {} | {} | {:.1f} | {:.1f} | {:.1f} | {:.1f}% |".format(
+            short_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    return "\n".join(lines) + "\n"
+
+
+def _counter_per_kernel(d: str, counter: str):
+    vals = {}
+    for r in _rows(d, "counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        vals.setdefault(short_name(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return vals
+
+
+def traffic(fetch_dir: str, write_dir: str, copy_bytes: int) -> dict:
+    """Calibrated HBM bytes per launch of each attention kernel."""
+    out = {}
+    for counter, d, key in (("FETCH_SIZE", fetch_dir, "read"), ("WRITE_SIZE", write_dir, "write")):
+        per = _counter_per_kernel(d, counter)
+        copies = [v for k, vs in per.items() if k.startswith("copy:") for v in vs]
+        probe = max(copies) if copies else None        # the big copy is the probe
+        factor = copy_bytes / (probe * 1024.0) if probe else None
+        out[f"{key}_calibration"] = {"probe_bytes": copy_bytes,
+                                     "counter_kib": probe, "factor": factor}
+        for k in KERNELS:
+            if k in per and factor:
+                out.setdefault(k, {})[f"{key}_bytes"] = statistics.median(per[k]) * 1024.0 * factor
+                out[k][f"{key}_counter_kib"] = statistics.median(per[k])
+    return out
+
+
+def main(argv):
+    if argv[0] == "stats":
+        text = stats_summary(argv[1], argv[3])
+        open(argv[2], "w").write(text)
+        print(text)
+    elif argv[0] == "traffic":
+        fetch_dir, write_dir, workload, out_path, cmd_f, cmd_w = argv[1:7]
+        copy_bytes = int(os.environ.get("FA_COPY_PROBE_BYTES", 512 << 20))
+        t = traffic(fetch_dir, write_dir, copy_bytes)
+        t.update({"workload": workload, "source_hash": source_hash(),
+                  "commands": {"FETCH_SIZE": cmd_f, "WRITE_SIZE": cmd_w}})
+        json.dump(t, open(out_path, "w"), indent=1)
+        print(json.dumps(t, indent=1))
+    else:
+        raise SystemExit(__doc__)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
