@@ -118,11 +118,10 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
 
   const int ntiles = (N + BQ - 1) / BQ;
   const int first = CAUSAL ? k0 / BQ : 0;
-  const uint8_t* mcol = MASKED ? mask + kb : nullptr;     // mask[qi][kb], stride T
+  // Column kb of the block mask: mask[qi][kb], stride T.
+  KeptTiles<BQ> kept(MASKED ? mask + kb : nullptr, (size_t)T_tiles, T_tiles);
   auto next_kept = [&](int i) {
-    if constexpr (MASKED) {
-      while (i < ntiles && mcol[(size_t)((i * BQ) / kMaskBlock) * T_tiles] == 0) ++i;
-    }
+    if constexpr (MASKED) return kept.next(i, lane);
     return i;
   };
 
@@ -422,11 +421,9 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
 
   const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
   const int ntiles = (kv_end + BC - 1) / BC;
-  const uint8_t* mrow = MASKED ? mask + (size_t)(q0 / kMaskBlock) * T_tiles : nullptr;
+  KeptTiles<BC> kept(MASKED ? mask + (size_t)(q0 / kMaskBlock) * T_tiles : nullptr, 1, T_tiles);
   auto next_kept = [&](int j) {
-    if constexpr (MASKED) {
-      while (j < ntiles && mrow[(j * BC) / kMaskBlock] == 0) ++j;
-    }
+    if constexpr (MASKED) return kept.next(j, lane);
     return j;
   };
   auto stage = [&](int j, int buf) {

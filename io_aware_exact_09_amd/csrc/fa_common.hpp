@@ -16,9 +16,8 @@
 //                                                  index of a C tile, so that
 //                                                  registers 8t..8t+7 of C are
 //                                                  directly an operand chunk)
-// Tiles that feed the C-shaped side are stored transposed in LDS with each
-// 16-group of the contraction index permuted (bits 2 and 3 swapped), so a
-// lane's 8 values are one contiguous 16-byte (bf16) read.
+// Operands of the C-shaped side that come from LDS are read from row-major
+// tiles with the transposing LDS load (trans_frag below).
 
 #pragma once
 
@@ -63,9 +62,23 @@ template <bool V> struct BoolTag {
   __device__ constexpr operator bool() const { return V; }
 };
 
-// Position of contraction index x inside its 16-group in a transposed tile.
-__device__ __forceinline__ constexpr int perm16(int x) {
-  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+// Value of lane l ^ 32 exchanged without a trip through LDS:
+// v_permlane32_swap_b32 swaps the upper 32 lanes of its first register with
+// the lower 32 lanes of its second, so with both holding x the pair becomes
+// (x of lanes 0-31 twice, x of lanes 32-63 twice).  The leading s_nop covers
+// the wait states the swap needs after a VALU write of its sources.
+__device__ __forceinline__ void swap_halves(float& a, float& b) {
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  float a = x, b = x;
+  swap_halves(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  float a = x, b = x;
+  swap_halves(a, b);
+  return a + b;
 }
 
 // ---------------------------------------------------------------------------
@@ -137,8 +150,17 @@ template <> struct Elem<float> {
 // ---------------------------------------------------------------------------
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
+// Every caller passes a wave-uniform base and size.  Saying so explicitly
+// keeps the descriptor in scalar registers: if the compiler cannot prove the
+// values uniform it wraps each buffer load in a per-lane loop over distinct
+// descriptors.
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
+  void* ub = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, 0, __builtin_amdgcn_readfirstlane(bytes),
+                                           0x00020000);
 }
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
@@ -355,6 +377,45 @@ __device__ __forceinline__ Elem<__bf16>::frag trans_frag_at(const unsigned char*
   f.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
   return f;
 }
+
+// Kept tiles along one row (stride 1) or one column (stride = row length) of
+// the 128 x 128 block mask, for tiles TILE wide (TILE divides 128).  The wave
+// fetches the mask 64 blocks at a time, one byte per lane, and keeps the
+// 64-bit ballot, so the tile loop touches global memory for the mask once
+// per 64 blocks instead of once per tile.
+template <int TILE>
+struct KeptTiles {
+  static_assert(kMaskBlock % TILE == 0, "tiles must divide the mask block");
+  static constexpr int TPB = kMaskBlock / TILE;
+  const uint8_t* p;
+  size_t stride;
+  int blocks;
+  int base = -64;          // first block of the cached ballot
+  uint64_t bits = 0;
+
+  __device__ KeptTiles(const uint8_t* p_, size_t stride_, int blocks_)
+      : p(p_), stride(stride_), blocks(blocks_) {}
+
+  // First kept tile >= j; blocks * TPB (past every tile) when none is left.
+  __device__ int next(int j, int lane) {
+    const int b0 = j / TPB;
+    for (int b = b0; b < blocks;) {
+      const int chunk = b & ~63;
+      if (chunk != base) {
+        base = chunk;
+        const int idx = chunk + lane;
+        bits = __ballot(idx < blocks && p[(size_t)idx * stride] != 0);
+      }
+      const uint64_t m = bits >> (b - chunk);
+      if (m) {
+        b += __builtin_ctzll(m);
+        return b == b0 ? j : b * TPB;
+      }
+      b = chunk + 64;
+    }
+    return blocks * TPB;
+  }
+};
 
 // Waves per SIMD each kernel is compiled for (two waves let one wave's
 // softmax arithmetic overlap the other's matrix work; the fp32 path at

@@ -76,11 +76,9 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
 
   const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
   const int ntiles = (kv_end + BC - 1) / BC;
-  const uint8_t* mrow = MASKED ? mask + (size_t)(q0 / kMaskBlock) * T_tiles : nullptr;
+  KeptTiles<BC> kept(MASKED ? mask + (size_t)(q0 / kMaskBlock) * T_tiles : nullptr, 1, T_tiles);
   auto next_kept = [&](int j) {
-    if constexpr (MASKED) {
-      while (j < ntiles && mrow[(j * BC) / kMaskBlock] == 0) ++j;
-    }
+    if constexpr (MASKED) return kept.next(j, lane);
     return j;
   };
   auto stage = [&](int j, int buf) {
@@ -148,16 +146,17 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     for (int h = 0; h < NH; ++h)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[h][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_tile = mx * c;
-    const bool grow = m_tile > m_run + kLazy;          // always true on the first kept tile
+    const float m_tile = max_xor32(mx) * c;
+    const bool grow = m_tile > m_run + kLazy;          // always true on a row's first kept key
     if (__any(grow)) {
-      const float m_new = grow ? m_tile : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run = -inf
+      // alpha = 1 on rows whose reference stays (also rows with nothing kept
+      // yet, whose m_run and m_tile are both -inf); 2^(-inf) = 0 on a row's
+      // first kept keys.
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.0f;
 #pragma unroll
       for (int b = 0; b < ND; ++b) oacc[b] *= alpha;
       l_run *= alpha;
-      m_run = m_new;
+      m_run = grow ? m_tile : m_run;
     }
     const float m_use = m_run == neg_inf() ? 0.f : m_run;
     // Row sum in fp32 from the unrounded probabilities (the log-sum-exp the
@@ -194,7 +193,7 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   }
 
   // ---- epilogue ----------------------------------------------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = sum_xor32(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   if (qrow < N) {
     T* Orow = O + head + (size_t)qrow * D;

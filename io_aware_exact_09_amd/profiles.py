@@ -3,8 +3,12 @@
     python -m io_aware_exact_09_amd.profiles stats <kernel_stats.csv> <out.md> "<command>"
     python -m io_aware_exact_09_amd.profiles traffic <fetch_dir> <write_dir> <workload> \
         <out.json> "<fetch command>" "<write command>"
+    python -m io_aware_exact_09_amd.profiles counters <out.md> <workload> \
+        <pass_dir>=<command> ...
 
-``stats`` condenses a ``--kernel-trace --stats`` run (per-kernel calls and
+``counters`` reads ``--pmc`` passes of the same bench command and tabulates,
+per kernel, the counters and the ratios derived from them (formulas in the
+output).  ``stats`` condenses a ``--kernel-trace --stats`` run (per-kernel calls and
 average duration).  ``traffic`` reads two ``--pmc FETCH_SIZE`` /
 ``--pmc WRITE_SIZE`` runs of ``bench.py --copy-probe``: the probe is a plain
 device-to-device copy of a known number of bytes, and the ratio of those bytes
@@ -96,6 +100,77 @@ def traffic(fetch_dir: str, write_dir: str, copy_bytes: int) -> dict:
     return out
 
 
+# Hardware constants of the MI355X used to normalise counters.
+N_XCD, N_CU, N_SIMD = 8, 256, 1024
+
+
+def counters_table(passes, workload: str) -> str:
+    """Per-kernel counter averages over dispatches, merged over passes."""
+    vals = {}
+    for d, _ in passes:
+        for r in _rows(d, "counter_collection.csv"):
+            k = short_name(r["Kernel_Name"])
+            if k not in KERNELS:
+                continue
+            vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    avg = {k: {c: statistics.mean(v) for c, v in cs.items()} for k, cs in vals.items()}
+
+    def ratio(k, f):
+        try:
+            return f(avg[k])
+        except (KeyError, ZeroDivisionError):
+            return None
+
+    derived = [
+        ("clock cycles per dispatch", "GRBM_GUI_ACTIVE / 8 (summed over the 8 XCDs)",
+         lambda c: c["GRBM_GUI_ACTIVE"] / N_XCD),
+        ("MFMA busy", "SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs)",
+         lambda c: c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] / N_XCD * N_SIMD)),
+        ("MFMA busy cycles per MFMA", "SQ_VALU_MFMA_BUSY_CYCLES / SQ_INSTS_MFMA",
+         lambda c: c["SQ_VALU_MFMA_BUSY_CYCLES"] / c["SQ_INSTS_MFMA"]),
+        ("VALU per MFMA", "(SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA",
+         lambda c: (c["SQ_INSTS_VALU"] - c["SQ_INSTS_MFMA"]) / c["SQ_INSTS_MFMA"]),
+        ("exp per MFMA", "SQ_INSTS_VALU_TRANS_F32 / SQ_INSTS_MFMA",
+         lambda c: c["SQ_INSTS_VALU_TRANS_F32"] / c["SQ_INSTS_MFMA"]),
+        ("LDS per MFMA", "SQ_INSTS_LDS / SQ_INSTS_MFMA",
+         lambda c: c["SQ_INSTS_LDS"] / c["SQ_INSTS_MFMA"]),
+        ("MFMA/VALU co-issue", "SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES",
+         lambda c: c["SQ_VALU_MFMA_COEXEC_CYCLES"] / c["SQ_VALU_MFMA_BUSY_CYCLES"]),
+        ("LDS bank conflicts per access", "SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE - SQ_LDS_BANK_CONFLICT)",
+         lambda c: c["SQ_LDS_BANK_CONFLICT"] / (c["SQ_LDS_IDX_ACTIVE"] - c["SQ_LDS_BANK_CONFLICT"])),
+        ("LDS busy", "SQ_LDS_IDX_ACTIVE / (cycles x 256 CUs)",
+         lambda c: c["SQ_LDS_IDX_ACTIVE"] / (c["GRBM_GUI_ACTIVE"] / N_XCD * N_CU)),
+        ("wave time waiting (any)", "SQ_WAIT_ANY / SQ_WAVE_CYCLES",
+         lambda c: c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"]),
+        ("wave time waiting to issue", "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES",
+         lambda c: c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"]),
+        ("wave time waiting to issue LDS", "SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES",
+         lambda c: c["SQ_WAIT_INST_LDS"] / c["SQ_WAVE_CYCLES"]),
+        ("wave time issuing", "SQ_ACTIVE_INST_ANY / SQ_WAVE_CYCLES",
+         lambda c: c["SQ_ACTIVE_INST_ANY"] / c["SQ_WAVE_CYCLES"]),
+        ("L2 hit rate", "TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum)",
+         lambda c: c["TCC_HIT_sum"] / (c["TCC_HIT_sum"] + c["TCC_MISS_sum"])),
+    ]
+    ks = [k for k in KERNELS if k in avg]
+    lines = [f"# rocprofv3 counters, workload `{workload}`", "",
+             "Averages over the profiled dispatches; SQ counters are summed over the chip by "
+             "rocprofv3, GRBM_GUI_ACTIVE over the 8 XCDs.", "",
+             "Commands (one `--pmc` pass each):", ""]
+    lines += [f"* `{cmd}`" for _, cmd in passes]
+    lines += ["", "| derived | formula | " + " | ".join(ks) + " |",
+              "|---|---|" + "---|" * len(ks)]
+    for name, formula, f in derived:
+        cells = []
+        for k in ks:
+            v = ratio(k, f)
+            cells.append("" if v is None else (f"{v:.0f}" if v > 100 else f"{v:.3f}"))
+        lines.append(f"| {name} | {formula} | " + " | ".join(cells) + " |")
+    lines += ["", "| counter | " + " | ".join(ks) + " |", "|---|" + "---|" * len(ks)]
+    for c in sorted({c for k in ks for c in avg[k]}):
+        lines.append(f"| {c} | " + " | ".join(f"{avg[k][c]:.4g}" if c in avg[k] else "" for k in ks) + " |")
+    return "\n".join(lines) + "\n"
+
+
 def main(argv):
     if argv[0] == "stats":
         text = stats_summary(argv[1], argv[3])
@@ -109,6 +184,12 @@ def main(argv):
                   "commands": {"FETCH_SIZE": cmd_f, "WRITE_SIZE": cmd_w}})
         json.dump(t, open(out_path, "w"), indent=1)
         print(json.dumps(t, indent=1))
+    elif argv[0] == "counters":
+        out_path, workload = argv[1], argv[2]
+        passes = [tuple(a.split("=", 1)) for a in argv[3:]]
+        text = counters_table(passes, workload)
+        open(out_path, "w").write(text)
+        print(text)
     else:
         raise SystemExit(__doc__)
 
