@@ -37,6 +37,11 @@ def common_flags() -> list[str]:
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA results and accumulators in VGPRs (operands may still come
+        # from AGPRs): the accumulators the VALU works on (S, dP) then need
+        # no copies out of AGPRs, which otherwise cost about one VALU
+        # instruction per accumulator register per tile in the dK/dV pass.
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-I", os.path.join(ROOT, "include"),
     ]
 

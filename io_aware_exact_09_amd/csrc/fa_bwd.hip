@@ -68,7 +68,8 @@ fa_bwd_delta_kernel(const T* __restrict__ O, const T* __restrict__ dO, float* __
 template <typename T>
 struct DkdvCfg {
   static constexpr int BK = 128;                         // keys per work-group
-  static constexpr int BQ = sizeof(T) == 2 ? 64 : 32;   // query rows per tile
+  static constexpr int BQ = sizeof(T) == 2 ? 64 : 32;   // query rows per compute tile
+  static constexpr int SQ = 2 * BQ;                      // query rows per staged tile
 };
 
 template <typename T, int D, bool CAUSAL, bool MASKED>
@@ -82,16 +83,19 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   using E = Elem<T>;
   using frag = typename E::frag;
   using Cfg = DkdvCfg<T>;
-  constexpr int BK = Cfg::BK, BQ = Cfg::BQ;
+  constexpr int BK = Cfg::BK, BQ = Cfg::BQ, SQ = Cfg::SQ;
   constexpr int NQH = BQ / 32;            // 32-row query halves per tile
   constexpr int NT = D / 16, ND = D / 32;
   constexpr uint32_t RB = Tile<T, D>::RB;
-  constexpr int TB = BQ * RB;             // bytes per Q or dO tile
+  constexpr int TB = BQ * RB;             // bytes per compute tile of Q or dO
+  constexpr int STB = SQ * RB;            // bytes per staged tile of Q or dO
 
-  // [buffer][Q, dO] tiles, double-buffered, plus per-row LSE*log2e and D.
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * TB];
-  __shared__ __attribute__((aligned(16))) float sL[2][BQ];   // +inf: no keys / past N
-  __shared__ __attribute__((aligned(16))) float sD[2][BQ];
+  // Two buffers of [Q, dO] tiles (distinct arrays, see pick()), plus per-row
+  // LSE*log2e and D.
+  __shared__ __attribute__((aligned(1024))) unsigned char lds0[2 * STB];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds1[2 * STB];
+  __shared__ __attribute__((aligned(16))) float sL[2][SQ];   // +inf: no keys / past N
+  __shared__ __attribute__((aligned(16))) float sD[2][SQ];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
@@ -114,12 +118,16 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
     const uint32_t off = (uint32_t)krow * RB + (16 * t + 8 * g) * sizeof(T);
     kf[t] = gload_frag<T>(rk, off);
     vf[t] = gload_frag<T>(rv, off);
+    to_agpr(kf[t]);
+    to_agpr(vf[t]);
   }
 
-  const int ntiles = (N + BQ - 1) / BQ;
-  const int first = CAUSAL ? k0 / BQ : 0;
+  // Staged tiles of SQ query rows, each run as two compute tiles of BQ rows
+  // (one barrier and one round of loads per SQ rows).
+  const int ntiles = (N + SQ - 1) / SQ;
+  const int first = CAUSAL ? k0 / SQ : 0;
   // Column kb of the block mask: mask[qi][kb], stride T.
-  KeptTiles<BQ> kept(MASKED ? mask + kb : nullptr, (size_t)T_tiles, T_tiles);
+  KeptTiles<SQ> kept(MASKED ? mask + kb : nullptr, (size_t)T_tiles, T_tiles);
   auto next_kept = [&](int i) {
     if constexpr (MASKED) return kept.next(i, lane);
     return i;
@@ -127,15 +135,15 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
 
   const rsrc_t rl = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
   const rsrc_t rd = make_rsrc(delta + (size_t)bh * N, (uint32_t)N * 4);
-  float lpre = 0.f, dpre = 0.f;     // row statistics of the tile in flight (threads < BQ)
+  float lpre = 0.f, dpre = 0.f;     // row statistics of the tile in flight (threads < SQ)
   int lrow_pre = 0;
-  auto stage = [&](int i, int buf) {
-    const int q0 = i * BQ;
+  auto stage = [&](int i, auto buf) {
+    const int q0 = i * SQ;
     const uint32_t left = (uint32_t)(N - q0) * RB;
-    unsigned char* base = smem + buf * 2 * TB;
-    stage_tile<T, D, BQ>(make_rsrc(Qh + (size_t)q0 * D, left), base, w, lane);
-    stage_tile<T, D, BQ>(make_rsrc(dOh + (size_t)q0 * D, left), base + TB, w, lane);
-    if (tid < BQ) {
+    unsigned char* base = pick(buf, lds0, lds1);
+    stage_tile<T, D, SQ>(make_rsrc(Qh + (size_t)q0 * D, left), base, w, lane);
+    stage_tile<T, D, SQ>(make_rsrc(dOh + (size_t)q0 * D, left), base + STB, w, lane);
+    if (tid < SQ) {
       lpre = buf_load_f32(rl, (uint32_t)(q0 + tid) * 4);   // raw; transformed when stored
       dpre = buf_load_f32(rd, (uint32_t)(q0 + tid) * 4);
       lrow_pre = q0 + tid;
@@ -150,11 +158,13 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
 
   // One tile iteration.  MASKED_TILE (the tile crosses this wave's causal
   // diagonal) is compile-time, so unmasked tiles carry no mask arithmetic.
-  auto tile = [&](auto mask_tag, auto buf_sel, int q0) {
+  auto tile = [&](auto mask_tag, auto buf_sel, int sub, int q0) {
     const int BUF = buf_sel;
     constexpr bool MASKED_TILE = decltype(mask_tag)::value;
-    const unsigned char* sQ = smem + BUF * 2 * TB;
-    const unsigned char* sdO = sQ + TB;
+    const unsigned char* sQ = pick(buf_sel, lds0, lds1) + sub * TB;
+    const unsigned char* sdO = sQ + STB;
+    const float* sLt = &sL[BUF][sub * BQ];
+    const float* sDt = &sD[BUF][sub * BQ];
       // The tile is processed as a pipeline of MFMA blocks:
       //   S/dP of query half 0 (NT/SB blocks of 2*SB MFMAs), S/dP of half 1,
       //   dV/dK of half 0 (2 blocks of 2*ND MFMAs), dV/dK of half 1.
@@ -171,11 +181,13 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
           if constexpr (sizeof(T) == 2) {
             const unsigned char* p = sQ + lo.row[t0 + t] + 32 * qh * RB;
             aq[t] = row_frag_at<T>(p);
-            ao[t] = row_frag_at<T>(p + TB);
+            ao[t] = row_frag_at<T>(p + STB);
           } else {
             aq[t] = row_frag<T, D>(sQ, 32 * qh + l32, t0 + t, g);
             ao[t] = row_frag<T, D>(sdO, 32 * qh + l32, t0 + t, g);
           }
+          to_agpr(aq[t]);
+          to_agpr(ao[t]);
         }
       };
       auto sdp_mma = [&](int t0, const frag* aq, const frag* ao, f32x16& sv, f32x16& dpv) {
@@ -191,8 +203,8 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
 #pragma unroll
         for (int a = a0; a < a1; ++a) {
           const int qi = 32 * qh + 8 * a + 4 * g;
-          const f32x4 lv = *reinterpret_cast<const f32x4*>(&sL[BUF][qi]);
-          const f32x4 dv = *reinterpret_cast<const f32x4*>(&sD[BUF][qi]);
+          const f32x4 lv = *reinterpret_cast<const f32x4*>(sLt + qi);
+          const f32x4 dv = *reinterpret_cast<const f32x4*>(sDt + qi);
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
             const int r = 4 * a + x;
@@ -216,12 +228,14 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
           if constexpr (sizeof(T) == 2) {
             const unsigned char* p0 = sQ + lo.tr[b][0] + 16 * (2 * qh + t) * RB;
             const unsigned char* p1 = sQ + lo.tr[b][1] + 16 * (2 * qh + t) * RB;
-            ot[b] = trans_frag_at(p0 + TB, p1 + TB);
+            ot[b] = trans_frag_at(p0 + STB, p1 + STB);
             qt[b] = trans_frag_at(p0, p1);
           } else {
             ot[b] = trans_frag<T, D>(sdO, b, 2 * qh + t, lane);
             qt[b] = trans_frag<T, D>(sQ, b, 2 * qh + t, lane);
           }
+          to_agpr(ot[b]);
+          to_agpr(qt[b]);
         }
       };
       auto dvdk_mma = [&](const frag* ot, const frag* qt, const frag& pf, const frag& df) {
@@ -306,28 +320,31 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   auto step = [&](auto buf_sel, int i, int in) {
     const int BUF = buf_sel;
     wait_global_loads();
-    if (tid < BQ) {
+    if (tid < SQ) {
       // Rows past N, and rows that keep no key (LSE = -inf), get P = 0.
       sL[BUF][tid] = (lrow_pre < N && lpre != neg_inf()) ? lpre * kLog2e : pos_inf();
       sD[BUF][tid] = dpre;
     }
     __syncthreads();
-    const int q0 = i * BQ;
-    if (in < ntiles) stage(in, BUF ^ 1);
-    if constexpr (sizeof(T) == 4) {
-      tile(BoolTag<CAUSAL>{}, buf_sel, q0);   // one body: the fp32 path needs every register
-    } else {
-      if (CAUSAL && q0 < kw + 31) tile(BoolTag<true>{}, buf_sel, q0);
-      else tile(BoolTag<false>{}, buf_sel, q0);
+    if (in < ntiles) stage(in, other(buf_sel));
+#pragma unroll 1
+    for (int sub = 0; sub < SQ / BQ; ++sub) {
+      const int q0 = i * SQ + sub * BQ;
+      if (q0 >= N) break;
+      if constexpr (sizeof(T) == 4) {
+        tile(BoolTag<CAUSAL>{}, buf_sel, sub, q0);   // one body: the fp32 path needs every register
+      } else {
+        if (CAUSAL && q0 < kw + 31) tile(BoolTag<true>{}, buf_sel, sub, q0);
+        else tile(BoolTag<false>{}, buf_sel, sub, q0);
+      }
     }
   };
 
   int i = next_kept(first);
-  if (i < ntiles) stage(i, 0);
-  if constexpr (CAUSAL && sizeof(T) == 2) {
+  if (i < ntiles) stage(i, IntTag<0>{});
+  if constexpr (sizeof(T) == 2) {
     // Two iterations per trip with the buffer index a compile-time constant,
-    // so the LDS offsets are immediates.  (The register allocator handles
-    // this shape well only for the causal instances.)
+    // so the LDS offsets are immediates.
     while (i < ntiles) {
       int in = next_kept(i + 1);
       step(IntTag<0>{}, i, in);
@@ -394,7 +411,9 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   constexpr uint32_t RB = Tile<T, D>::RB;
   constexpr int TB = BC * RB;
 
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * TB];   // [buf][K, V]
+  // Two buffers of [K, V] tiles (distinct arrays, see pick()).
+  __shared__ __attribute__((aligned(1024))) unsigned char lds0[2 * TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds1[2 * TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
@@ -426,10 +445,10 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
     if constexpr (MASKED) return kept.next(j, lane);
     return j;
   };
-  auto stage = [&](int j, int buf) {
+  auto stage = [&](int j, auto buf) {
     const int kv0 = j * BC;
     const uint32_t left = (uint32_t)(N - kv0) * RB;
-    unsigned char* base = smem + buf * 2 * TB;
+    unsigned char* base = pick(buf, lds0, lds1);
     stage_tile<T, D, BC>(make_rsrc(Kh + (size_t)kv0 * D, left), base, w, lane);
     stage_tile<T, D, BC>(make_rsrc(Vh + (size_t)kv0 * D, left), base + TB, w, lane);
   };
@@ -440,11 +459,13 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
 
   // Precomputed operand offsets when the register budget of two waves per
   // SIMD allows it (bf16, d = 64); otherwise addresses are formed per read.
+  // bf16, d = 64 also takes compile-time LDS buffers (loop unrolled by two).
+  // d = 128 has no register room for either at two waves per SIMD.
   constexpr bool USE_LO = sizeof(T) == 2 && D == 64;
   LaneOffsets<T, D> lo;
   if constexpr (USE_LO) lo.init(lane);
   int j = next_kept(0);
-  if (j < ntiles) stage(j, 0);
+  if (j < ntiles) stage(j, IntTag<0>{});
   wait_global_loads();
   const float lse2 = (qrow < N && lrow != neg_inf()) ? lrow * kLog2e : pos_inf();
 
@@ -454,7 +475,7 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   auto tile = [&](auto mask_sel, auto buf_sel, int kv0) {
     const bool MASKED_TILE = mask_sel;
     const int BUF = buf_sel;
-    const unsigned char* sK = smem + BUF * 2 * TB;
+    const unsigned char* sK = pick(buf_sel, lds0, lds1);
     const unsigned char* sV = sK + TB;
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
@@ -481,6 +502,7 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
           s = E::mma(ak[t], qf[t0 + t], s);
           dp = E::mma(av[t], of[t0 + t], dp);
         }
+        if constexpr (USE_LO) sched_fence();
       }
       // Register r holds key kv0 + 4g + 32h + 8(r/4) + r%4.
       const int lim = (CAUSAL ? min(N, qrow + 1) : N) - kv0 - 4 * g - 32 * h;
@@ -504,6 +526,7 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
         }
 #pragma unroll
         for (int b = 0; b < ND; ++b) dqacc[b] = E::mma(kt[b], df, dqacc[b]);
+        if constexpr (USE_LO) sched_fence();
       }
     }
   };
@@ -512,7 +535,7 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
     wait_global_loads();
     __syncthreads();
     const int kv0 = j * BC;
-    if (jn < ntiles) stage(jn, BUF ^ 1);
+    if (jn < ntiles) stage(jn, other(buf_sel));
     const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > q0 + 32 * w);
     if constexpr (sizeof(T) == 2 && D == 64) {
       // Separate masked / unmasked bodies where the registers allow it.
@@ -522,7 +545,7 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
       tile(need_mask, buf_sel, kv0);
     }
   };
-  if constexpr (CAUSAL && sizeof(T) == 2 && D == 64) {
+  if constexpr (sizeof(T) == 2 && D == 64) {
     while (j < ntiles) {   // two tiles per trip, buffer index compile-time
       int jn = next_kept(j + 1);
       step(IntTag<0>{}, j, jn);

@@ -62,6 +62,23 @@ template <bool V> struct BoolTag {
   __device__ constexpr operator bool() const { return V; }
 };
 
+// Double-buffered LDS tiles are two distinct __shared__ arrays, and loops
+// that alternate between them are unrolled by two so the buffer is a
+// compile-time choice (pick with an IntTag).  Then the compiler can tell that
+// an LDS read of one buffer does not touch the other buffer, which the
+// direct-to-LDS loads of the next tile are filling: with a single array (or a
+// runtime choice) it makes each transposing LDS read wait until all of those
+// loads have landed.
+template <int V>
+__device__ __forceinline__ unsigned char* pick(IntTag<V>, unsigned char* b0, unsigned char* b1) {
+  return V == 0 ? b0 : b1;
+}
+__device__ __forceinline__ unsigned char* pick(int v, unsigned char* b0, unsigned char* b1) {
+  return v ? b1 : b0;
+}
+template <int V> __device__ __forceinline__ constexpr IntTag<V ^ 1> other(IntTag<V>) { return {}; }
+__device__ __forceinline__ int other(int v) { return v ^ 1; }
+
 // Value of lane l ^ 32 exchanged without a trip through LDS:
 // v_permlane32_swap_b32 swaps the upper 32 lanes of its first register with
 // the lower 32 lanes of its second, so with both holding x the pair becomes
@@ -192,6 +209,17 @@ __device__ __forceinline__ void interleave() {
   for (int i = 0; i < MFMAS; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
     __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);   // VALU
+  }
+}
+
+// Pin an MFMA operand fragment to the accumulation registers (AGPRs).
+template <typename F>
+__device__ __forceinline__ void to_agpr(F& f) {
+  if constexpr (sizeof(f) == 16) {
+    asm("" : "+a"(f.v));
+  } else {
+    asm("" : "+a"(f.lo));
+    asm("" : "+a"(f.hi));
   }
 }
 

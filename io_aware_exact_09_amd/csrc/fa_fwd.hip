@@ -53,8 +53,9 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   constexpr uint32_t RB = Tile<T, D>::RB;  // bytes per row
   constexpr int TB = BC * RB;              // bytes per K or V tile
 
-  // [buffer][K, V] tiles, double-buffered.
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * TB];
+  // Two buffers of [K, V] tiles (distinct arrays, see pick()).
+  __shared__ __attribute__((aligned(1024))) unsigned char lds0[2 * TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds1[2 * TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
@@ -81,10 +82,10 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     if constexpr (MASKED) return kept.next(j, lane);
     return j;
   };
-  auto stage = [&](int j, int buf) {
+  auto stage = [&](int j, auto buf) {
     const int kv0 = j * BC;
     const uint32_t left = (uint32_t)(N - kv0) * RB;
-    unsigned char* base = smem + buf * 2 * TB;
+    unsigned char* base = pick(buf, lds0, lds1);
     stage_tile<T, D, BC>(make_rsrc(Kh + (size_t)kv0 * D, left), base, w, lane);
     stage_tile<T, D, BC>(make_rsrc(Vh + (size_t)kv0 * D, left), base + TB, w, lane);
   };
@@ -95,16 +96,19 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   float m_run = neg_inf();   // running max of S*c (log2 domain), same in both lane halves
   float l_run = 0.f;         // this lane's partial row sum
 
-  int j = next_kept(0);
-  int buf = 0;
-  if (j < ntiles) stage(j, 0);
-  while (j < ntiles) {
-    wait_global_loads();             // this wave's part of tile j has landed
-    __syncthreads();                 // all of tile j is in LDS; buffer buf^1 is free
-    const int kv0 = j * BC;
-    const int jn = next_kept(j + 1);
-    if (jn < ntiles) stage(jn, buf ^ 1);   // in flight while this tile is computed
-    const unsigned char* sK = smem + buf * 2 * TB;
+  // bf16, d = 64: compile-time LDS buffers (loop unrolled by two) and
+  // precomputed operand offsets.  d = 128 keeps a runtime buffer index: at
+  // two waves per SIMD its registers have no room for either, and measured
+  // slower with them.
+  constexpr bool kCt = sizeof(T) == 2 && D == 64;
+  LaneOffsets<T, D> lo;
+  if constexpr (kCt) lo.init(lane);
+
+  // One kept tile in LDS buffer `buf` (an IntTag where compile-time).
+  // `first`: no earlier kept tile, so O and l are still zero and need no
+  // rescaling.
+  auto tile = [&](auto buf_tag, int kv0, bool first) {
+    const unsigned char* sK = pick(buf_tag, lds0, lds1);
     const unsigned char* sV = sK + TB;
 
     // ---- S^T = K_j Q^T -------------------------------------------------
@@ -115,7 +119,10 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     for (int h = 0; h < NH; ++h) {
       frag ak[NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) ak[t] = row_frag<T, D>(sK, 32 * h + l32, t, g);
+      for (int t = 0; t < NT; ++t) {
+        if constexpr (kCt) ak[t] = row_frag_at<T>(sK + lo.row[t] + 32 * h * RB);
+        else ak[t] = row_frag<T, D>(sK, 32 * h + l32, t, g);
+      }
       sched_fence();
       s[h] = f32x16{};
 #pragma unroll
@@ -149,13 +156,15 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     const float m_tile = max_xor32(mx) * c;
     const bool grow = m_tile > m_run + kLazy;          // always true on a row's first kept key
     if (__any(grow)) {
-      // alpha = 1 on rows whose reference stays (also rows with nothing kept
-      // yet, whose m_run and m_tile are both -inf); 2^(-inf) = 0 on a row's
-      // first kept keys.
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.0f;
+      if (!first) {
+        // alpha = 1 on rows whose reference stays (also rows with nothing
+        // kept yet, whose m_run and m_tile are both -inf); 2^(-inf) = 0 on a
+        // row's first kept keys.
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.0f;
 #pragma unroll
-      for (int b = 0; b < ND; ++b) oacc[b] *= alpha;
-      l_run *= alpha;
+        for (int b = 0; b < ND; ++b) oacc[b] *= alpha;
+        l_run *= alpha;
+      }
       m_run = grow ? m_tile : m_run;
     }
     const float m_use = m_run == neg_inf() ? 0.f : m_run;
@@ -183,13 +192,40 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     for (int b = 0; b < ND; ++b) {
       frag av[2 * NH];
 #pragma unroll
-      for (int cc = 0; cc < 2 * NH; ++cc) av[cc] = trans_frag<T, D>(sV, b, cc, lane);
+      for (int cc = 0; cc < 2 * NH; ++cc) {
+        if constexpr (kCt)
+          av[cc] = trans_frag_at(sV + lo.tr[b][0] + 16 * cc * RB, sV + lo.tr[b][1] + 16 * cc * RB);
+        else
+          av[cc] = trans_frag<T, D>(sV, b, cc, lane);
+      }
       sched_fence();
 #pragma unroll
       for (int cc = 0; cc < 2 * NH; ++cc) oacc[b] = E::mma(av[cc], pf[cc >> 1][cc & 1], oacc[b]);
     }
-    buf ^= 1;
+  };
+
+  // Wait for kept tile j (buffer buf_tag), prefetch the next kept tile into
+  // the other buffer, then run the tile.
+  int j = next_kept(0);
+  bool first = true;
+  auto step = [&](auto buf_tag) {
+    wait_global_loads();             // this wave's part of tile j has landed
+    __syncthreads();                 // all of tile j is in LDS; the other buffer is free
+    const int jn = next_kept(j + 1);
+    if (jn < ntiles) stage(jn, other(buf_tag));   // in flight while this tile is computed
+    tile(buf_tag, j * BC, first);
+    first = false;
     j = jn;
+  };
+  if (j < ntiles) stage(j, IntTag<0>{});
+  if constexpr (kCt) {
+    while (j < ntiles) {   // two tiles per trip: the buffer index is compile-time
+      step(IntTag<0>{});
+      if (j >= ntiles) break;
+      step(IntTag<1>{});
+    }
+  } else {
+    for (int buf = 0; j < ntiles; buf ^= 1) step(buf);
   }
 
   // ---- epilogue ----------------------------------------------------------------

@@ -148,6 +148,18 @@ def counters_table(passes, workload: str) -> str:
          lambda c: c["SQ_WAIT_INST_LDS"] / c["SQ_WAVE_CYCLES"]),
         ("wave time issuing", "SQ_ACTIVE_INST_ANY / SQ_WAVE_CYCLES",
          lambda c: c["SQ_ACTIVE_INST_ANY"] / c["SQ_WAVE_CYCLES"]),
+        ("VALU issue time per SIMD", "4 SQ_ACTIVE_INST_VALU / (cycles x 1024 SIMDs)",
+         lambda c: 4 * c["SQ_ACTIVE_INST_VALU"] / (c["GRBM_GUI_ACTIVE"] / N_XCD * N_SIMD)),
+        ("LDS issue time per SIMD", "4 SQ_ACTIVE_INST_LDS / (cycles x 1024 SIMDs)",
+         lambda c: 4 * c["SQ_ACTIVE_INST_LDS"] / (c["GRBM_GUI_ACTIVE"] / N_XCD * N_SIMD)),
+        ("integer VALU per MFMA", "SQ_INSTS_VALU_INT32 / SQ_INSTS_MFMA",
+         lambda c: c["SQ_INSTS_VALU_INT32"] / c["SQ_INSTS_MFMA"]),
+        ("convert VALU per MFMA", "SQ_INSTS_VALU_CVT / SQ_INSTS_MFMA",
+         lambda c: c["SQ_INSTS_VALU_CVT"] / c["SQ_INSTS_MFMA"]),
+        ("fp32 FMA per MFMA", "SQ_INSTS_VALU_FMA_F32 / SQ_INSTS_MFMA",
+         lambda c: c["SQ_INSTS_VALU_FMA_F32"] / c["SQ_INSTS_MFMA"]),
+        ("scalar ALU per MFMA", "SQ_INSTS_SALU / SQ_INSTS_MFMA",
+         lambda c: c["SQ_INSTS_SALU"] / c["SQ_INSTS_MFMA"]),
         ("L2 hit rate", "TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum)",
          lambda c: c["TCC_HIT_sum"] / (c["TCC_HIT_sum"] + c["TCC_MISS_sum"])),
     ]
