@@ -462,8 +462,11 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   // bf16, d = 64 also takes compile-time LDS buffers (loop unrolled by two).
   // d = 128 has no register room for either at two waves per SIMD.
   constexpr bool USE_LO = sizeof(T) == 2 && D == 64;
+  constexpr bool USE_XO = sizeof(T) == 2 && D == 128;
   LaneOffsets<T, D> lo;
   if constexpr (USE_LO) lo.init(lane);
+  XorOffsets<__bf16, D> xo;
+  if constexpr (USE_XO) xo.init(lane);
   int j = next_kept(0);
   if (j < ntiles) stage(j, IntTag<0>{});
   wait_global_loads();
@@ -477,6 +480,7 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
     const int BUF = buf_sel;
     const unsigned char* sK = pick(buf_sel, lds0, lds1);
     const unsigned char* sV = sK + TB;
+    if constexpr (USE_XO) xo.refresh();
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       // Operands in sub-batches of SB chunks (register budget of two waves
@@ -488,8 +492,9 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
         frag ak[SB], av[SB];
 #pragma unroll
         for (int t = 0; t < SB; ++t) {
-          if constexpr (USE_LO) {
-            const unsigned char* p = sK + lo.row[t0 + t] + 32 * h * RB;
+          if constexpr (USE_LO || USE_XO) {
+            const unsigned char* p =
+                sK + (USE_LO ? lo.row[t0 + t] : xo.row_at(t0 + t)) + 32 * h * RB;
             ak[t] = row_frag_at<T>(p);
             av[t] = row_frag_at<T>(p + TB);
           } else {
@@ -521,6 +526,8 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
         for (int b = 0; b < ND; ++b) {
           if constexpr (USE_LO)
             kt[b] = trans_frag_at(sK + lo.tr[b][0] + 16 * cc * RB, sK + lo.tr[b][1] + 16 * cc * RB);
+          else if constexpr (USE_XO)
+            kt[b] = trans_frag_at(sK + xo.tr_at(b, 0) + 16 * cc * RB, sK + xo.tr_at(b, 1) + 16 * cc * RB);
           else
             kt[b] = trans_frag<T, D>(sK, b, cc, lane);
         }

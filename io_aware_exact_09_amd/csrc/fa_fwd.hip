@@ -256,6 +256,239 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong forward: bf16 without a block mask.
+//
+// Eight waves, two per SIMD.  Group G = w / 4 owns query rows q0 + 128 G ..
+// q0 + 128 G + 127 (wave w % 4 owns 32 of them, laid out as above), and both
+// groups walk the same K/V tiles, kept in a ring of three LDS slots.  Time is
+// cut into phases by work-group barriers.  In each phase one group runs its
+// matrix work (S^T of tile t, and O^T += V^T P^T of tile t - 1) while the
+// other runs the softmax of its latest scores on the VALU; the roles swap
+// every phase, so each SIMD has one wave feeding the matrix cores while the
+// other does the exponentials.  Step s (phases 2s and 2s+1):
+//   group 0:  matrix(s)     | softmax(s)
+//   group 1:  softmax(s-1)  | matrix(s)
+// At the start of step s every wave issues its part of the loads of tile s+1
+// into slot (s+1) % 3, whose previous tile (s-2) was last read in step s-1,
+// and waits for them at the end of the step, before the barrier after which
+// tile s+1 is first read.  The loop is unrolled by three steps so the slots
+// are compile-time choices of three distinct arrays (see pick()).
+// ---------------------------------------------------------------------------
+template <int V>
+__device__ __forceinline__ unsigned char* pick3(IntTag<V>, unsigned char* a, unsigned char* b,
+                                                unsigned char* c) {
+  return V == 0 ? a : (V == 1 ? b : c);
+}
+
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(2 * kThreads)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+fa_fwd_pp_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+                 T* __restrict__ O, float* __restrict__ LSE, int BH, int N,
+                 float c /* scale*log2e, > 0 */) {
+  static_assert(sizeof(T) == 2, "bf16 only");
+  using E = Elem<T>;
+  using frag = typename E::frag;
+  constexpr int BR = 256, BC = 64;
+  constexpr int NH = BC / 32, NT = D / 16, ND = D / 32;
+  constexpr uint32_t RB = Tile<T, D>::RB;
+  constexpr int TB = BC * RB;              // bytes per K or V tile
+
+  __shared__ __attribute__((aligned(1024))) unsigned char slot0[2 * TB];   // [K, V]
+  __shared__ __attribute__((aligned(1024))) unsigned char slot1[2 * TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char slot2[2 * TB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int G = w >> 2, wg = w & 3;
+  const int nqb = (N + BR - 1) / BR;
+  const BlockCoord bc = map_block(blockIdx.x, nqb, BH, CAUSAL, true);
+  const int bh = bc.bh, q0 = bc.blk * BR;
+  const size_t head = (size_t)bh * N * D;
+  const T* Kh = K + head;
+  const T* Vh = V + head;
+  const int row0 = q0 + 128 * G + 32 * wg;     // this wave's first row
+  const int qrow = row0 + l32;
+
+  const rsrc_t rq = make_rsrc(Q + head, (uint32_t)N * RB);
+  frag qf[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    qf[t] = gload_frag<T>(rq, (uint32_t)qrow * RB + (16 * t + 8 * g) * sizeof(T));
+
+  // Tiles of the work-group, and of this wave's group (causal: the first
+  // group's rows end 128 keys earlier).
+  const int ntiles = ((CAUSAL ? min(N, q0 + BR) : N) + BC - 1) / BC;
+  const int gtiles = ((CAUSAL ? min(N, q0 + 128 * (G + 1)) : N) + BC - 1) / BC;
+
+  auto stage = [&](int t, auto sl) {
+    const int kv0 = t * BC;
+    const uint32_t left = (uint32_t)(N - kv0) * RB;
+    unsigned char* base = pick3(sl, slot0, slot1, slot2);
+    stage_tile<T, D, BC, 8>(make_rsrc(Kh + (size_t)kv0 * D, left), base, w, lane);
+    stage_tile<T, D, BC, 8>(make_rsrc(Vh + (size_t)kv0 * D, left), base + TB, w, lane);
+  };
+
+  LaneOffsets<T, D> lo;
+  lo.init(lane);
+  f32x16 oacc[ND];
+#pragma unroll
+  for (int b = 0; b < ND; ++b) oacc[b] = f32x16{};
+  f32x16 sc[NH];             // scores of the tile between its matrix and softmax phases
+  frag pf[NH][2];            // probabilities of the tile between its softmax and P V
+  float m_run = neg_inf();   // running reference max of S*c (log2 domain)
+  float l_run = 0.f;         // this lane's partial row sum
+
+  // V^T operands of the tile whose P was produced last: blocks 0 .. NBP-1
+  // are read during the softmax phase, so the next matrix phase starts on
+  // MFMAs instead of LDS latency; the rest are read behind those MFMAs.
+  constexpr int NBP = ND / 2;
+  frag vpre[NBP][2 * NH];
+  auto read_v = [&](auto vs) {
+    const unsigned char* sV = pick3(vs, slot0, slot1, slot2) + TB;
+#pragma unroll
+    for (int b = 0; b < NBP; ++b)
+#pragma unroll
+      for (int cc = 0; cc < 2 * NH; ++cc)
+        vpre[b][cc] =
+            trans_frag_at(sV + lo.tr[b][0] + 16 * cc * RB, sV + lo.tr[b][1] + 16 * cc * RB);
+  };
+
+  // Matrix phase of step s: O^T += V^T P^T of tile s - 1 (from slot VS),
+  // then S^T of tile s (from slot KS); each batch of LDS operands is read
+  // in full before its MFMAs.
+  auto matrix = [&](auto ks, auto vs, int s) {
+    const unsigned char* sK = pick3(ks, slot0, slot1, slot2);
+    const unsigned char* sV = pick3(vs, slot0, slot1, slot2) + TB;
+    if (s >= 1 && s - 1 < gtiles) {
+      frag vr[ND - NBP][2 * NH];
+#pragma unroll
+      for (int b = NBP; b < ND; ++b)
+#pragma unroll
+        for (int cc = 0; cc < 2 * NH; ++cc)
+          vr[b - NBP][cc] =
+              trans_frag_at(sV + lo.tr[b][0] + 16 * cc * RB, sV + lo.tr[b][1] + 16 * cc * RB);
+      sched_fence();
+#pragma unroll
+      for (int b = 0; b < ND; ++b)
+#pragma unroll
+        for (int cc = 0; cc < 2 * NH; ++cc)
+          oacc[b] = E::mma(b < NBP ? vpre[b][cc] : vr[b - NBP][cc], pf[cc >> 1][cc & 1], oacc[b]);
+    }
+    if (s < gtiles) {
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        frag ak[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) ak[t] = row_frag_at<T>(sK + lo.row[t] + 32 * h * RB);
+        sched_fence();   // all reads of the batch first, then its MFMA chain
+        sc[h] = f32x16{};
+#pragma unroll
+        for (int t = 0; t < NT; ++t) sc[h] = E::mma(ak[t], qf[t], sc[h]);
+      }
+    }
+  };
+
+  // Softmax phase for tile t: mask, lazy reference max, O/l rescale, P.
+  // Register r of half h holds key kv0 + 4g + 32h + 8(r/4) + r%4.
+  auto softmax = [&](int t, auto vs) {
+    if (t < 0 || t >= gtiles) return;
+    read_v(vs);
+    const int kv0 = t * BC;
+    if ((kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > row0)) {
+      const int lim = (CAUSAL ? min(N, qrow + 1) : N) - kv0 - 4 * g;
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * h + 8 * (r >> 2) + (r & 3) >= lim) sc[h][r] = neg_inf();
+    }
+    float mx = neg_inf();
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[h][r]);
+    const float m_tile = max_xor32(mx) * c;
+    const bool grow = m_tile > m_run + kLazy;
+    if (__any(grow)) {
+      if (t > 0) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.0f;
+#pragma unroll
+        for (int b = 0; b < ND; ++b) oacc[b] *= alpha;
+        l_run *= alpha;
+      }
+      m_run = grow ? m_tile : m_run;
+    }
+    const float m_use = m_run == neg_inf() ? 0.f : m_run;
+    float psum[NH][4] = {};
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sc[h][r] = __builtin_amdgcn_exp2f(fmaf(sc[h][r], c, -m_use));
+        psum[h][r & 3] += sc[h][r];
+      }
+      pf[h][0] = E::from_c(sc[h], 0);
+      pf[h][1] = E::from_c(sc[h], 1);
+    }
+#pragma unroll
+    for (int h = 0; h < NH; ++h) l_run += (psum[h][0] + psum[h][1]) + (psum[h][2] + psum[h][3]);
+  };
+
+  // Step s with slot of tile s = KS (compile-time); the softmax phase of tile
+  // t also reads the V operands of tile t, so it takes that tile's slot.
+  auto step = [&](auto ks, int s) {
+    constexpr int KS = decltype(ks)::value;
+    constexpr IntTag<(KS + 2) % 3> vs{};    // slot of tile s - 1
+    constexpr IntTag<(KS + 1) % 3> ns{};    // slot of tile s + 1
+    if (s + 1 < ntiles) stage(s + 1, ns);
+    if (G == 0) matrix(ks, vs, s); else softmax(s - 1, vs);
+    // Phase boundary only: no data changes hands here, so a bare barrier
+    // (__syncthreads would first wait for the tile loads just issued).
+    __builtin_amdgcn_s_barrier();
+    if (G == 0) softmax(s, ks); else matrix(ks, vs, s);
+    wait_global_loads();
+    __syncthreads();
+  };
+
+  stage(0, IntTag<0>{});
+  wait_global_loads();
+  __syncthreads();
+  for (int s = 0; s <= ntiles;) {
+    step(IntTag<0>{}, s++);
+    if (s > ntiles) break;
+    step(IntTag<1>{}, s++);
+    if (s > ntiles) break;
+    step(IntTag<2>{}, s++);
+  }
+
+  const float l_tot = sum_xor32(l_run);
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  if (qrow < N) {
+    T* Orow = O + head + (size_t)qrow * D;
+#pragma unroll
+    for (int b = 0; b < ND; ++b)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        E::store4(Orow + 32 * b + 8 * a + 4 * g, oacc[b][4 * a] * inv, oacc[b][4 * a + 1] * inv,
+                  oacc[b][4 * a + 2] * inv, oacc[b][4 * a + 3] * inv);
+    if (g == 0)
+      LSE[(size_t)bh * N + qrow] =
+          l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : neg_inf();
+  }
+}
+
+template <typename T, int D, bool CAUSAL>
+static hipError_t launch_fwd_pp(const FwdArgs& a) {
+  const int nqb = (a.N + 255) / 256;
+  hipLaunchKernelGGL((fa_fwd_pp_kernel<T, D, CAUSAL>), dim3(nqb * a.BH), dim3(2 * kThreads), 0,
+                     a.stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                     static_cast<const T*>(a.v), static_cast<T*>(a.o), a.lse, a.BH, a.N,
+                     score_coef(a.scale));
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 static hipError_t launch_fwd_d(const FwdArgs& a) {
   if (a.causal) return a.mask ? launch_fwd_t<T, D, true, true>(a) : launch_fwd_t<T, D, true, false>(a);
@@ -263,6 +496,10 @@ static hipError_t launch_fwd_d(const FwdArgs& a) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a) {
+  // d = 128 without a block mask: the ping-pong kernel.  (At d = 64 the
+  // four-wave kernel runs three waves per SIMD and measured faster.)
+  if (a.bf16 && !a.mask && a.d == 128)
+    return a.causal ? launch_fwd_pp<__bf16, 128, true>(a) : launch_fwd_pp<__bf16, 128, false>(a);
   if (a.bf16) return a.d == 64 ? launch_fwd_d<__bf16, 64>(a) : launch_fwd_d<__bf16, 128>(a);
   return a.d == 64 ? launch_fwd_d<float, 64>(a) : launch_fwd_d<float, 128>(a);
 }
