@@ -50,6 +50,9 @@ SMALL = [
     (256, 64, "bf16", True, None), (256, 128, "bf16", True, None),
     (384, 128, "bf16", False, None), (384, 64, "fp32", False, None),
     (1000, 64, "bf16", True, "rand"), (1000, 128, "bf16", False, None),
+    # bf16 d = 128 without a mask runs the ping-pong forward: ragged and tiny N
+    (17, 128, "bf16", True, None), (300, 128, "bf16", True, None),
+    (513, 128, "bf16", True, None), (200, 128, "bf16", False, None),
 ]
 
 
