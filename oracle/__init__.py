@@ -26,6 +26,7 @@ from .attention import (  # noqa: F401
     key_rows,
     kept_pairs,
 )
+from . import dropout  # noqa: F401
 from .online import (  # noqa: F401
     merge_stats,
     tiled_forward_rescaled,

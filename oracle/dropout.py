@@ -1,0 +1,121 @@
+"""Attention with dropout on the probabilities: plain fp64 reference.
+
+TEST INFRASTRUCTURE (see the package docstring): never called by the product
+path.
+
+[FA-guide] "Temel fikirler" lists dropout among the operations the method
+fuses into its one kernel next to the matrix products, masking and softmax;
+the pages say nothing more about it.  Readings taken here (the plainest ones
+the rest of the pages support):
+
+  * Dropout acts on the attention probabilities: with keep mask Z (Z_ij in
+    {0, 1}, kept with probability 1 - p) and M = Z / (1 - p),
+        O = (P * M) V.
+    The softmax statistics (row max, row sum, LSE) are those of the
+    undropped P, so LSE is unchanged by dropout.
+  * Backward, by the chain rule through the same formula:
+        dV = (P * M)^T dO
+        dP = (dO V^T) * M
+        D_i = sum_k dO_ik O_ik      (still equals sum_j P_ij dP_ij)
+        dS = P * (dP - D 1^T),  dQ = scale dS K,  dK = scale dS^T Q.
+  * The mask is not stored: forward and backward regenerate it from a
+    counter-based generator, Philox4x32 with 10 rounds (Salmon, Moraes, Dror,
+    Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011).  Element
+    (i, j) of head bh (= b H + h) takes word j mod 4 of
+        Philox4x32-10(counter = (j // 4, i, bh, 0), key = (seed mod 2^32,
+                      seed // 2^32))
+    and is kept iff that word is >= T = floor(p 2^32) (so p = 0 keeps all).
+
+The generator is written from its published definition below, in numpy
+uint64 arithmetic; nothing is shared with the GPU library.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import _f64, _softmax_rows, keep_matrix, MASK_BLOCK
+
+# Philox4x32 constants from the paper: the two round multipliers and the two
+# Weyl increments of the key schedule.
+PHILOX_M0 = 0xD2511F53
+PHILOX_M1 = 0xCD9E8D57
+PHILOX_W0 = 0x9E3779B9
+PHILOX_W1 = 0xBB67AE85
+MASK32 = 0xFFFFFFFF
+
+
+def philox4x32(ctr, key, rounds: int = 10):
+    """Philox4x32-R on arrays.
+
+    ctr: four uint32 arrays (broadcastable), key: two uint32 values or
+    arrays.  One round maps (c0, c1, c2, c3) with key (k0, k1) to
+        (hi(M1 c2) ^ c1 ^ k0,  lo(M1 c2),  hi(M0 c0) ^ c3 ^ k1,  lo(M0 c0))
+    where hi/lo are the upper/lower 32 bits of the 64-bit product; between
+    rounds the key advances by (W0, W1) modulo 2^32.  Returns four uint32
+    arrays.
+    """
+    c0, c1, c2, c3 = (np.asarray(c, dtype=np.uint64) & MASK32 for c in ctr)
+    k0 = np.uint64(int(key[0]) & MASK32)
+    k1 = np.uint64(int(key[1]) & MASK32)
+    for r in range(rounds):
+        if r > 0:
+            k0 = np.uint64((int(k0) + PHILOX_W0) & MASK32)
+            k1 = np.uint64((int(k1) + PHILOX_W1) & MASK32)
+        p0 = c0 * np.uint64(PHILOX_M0)          # < 2^64: no overflow
+        p1 = c2 * np.uint64(PHILOX_M1)
+        hi0, lo0 = p0 >> np.uint64(32), p0 & np.uint64(MASK32)
+        hi1, lo1 = p1 >> np.uint64(32), p1 & np.uint64(MASK32)
+        c0, c1, c2, c3 = hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0
+    return tuple(x.astype(np.uint32) for x in (c0, c1, c2, c3))
+
+
+def threshold(p: float) -> int:
+    """Integer keep threshold T = floor(p 2^32) (clamped to 2^32 - 1)."""
+    if not (0.0 <= p < 1.0):
+        raise ValueError("dropout probability must lie in [0, 1)")
+    return min(int(np.floor(p * 4294967296.0)), MASK32)
+
+
+def keep_mask(bh: int, rows, cols, p: float, seed: int) -> np.ndarray:
+    """Boolean keep mask Z[rows, cols] of head bh (see the module docstring)."""
+    rows = np.asarray(rows, dtype=np.uint64)[:, None]
+    cols = np.asarray(cols, dtype=np.uint64)[None, :]
+    words = philox4x32((cols >> np.uint64(2), rows, np.full_like(cols, bh), np.zeros_like(cols)),
+                       (seed & MASK32, (seed >> 32) & MASK32))
+    w = np.stack(np.broadcast_arrays(*words), axis=-1)          # [rows, cols, 4]
+    pick = (cols & np.uint64(3)).astype(np.int64)
+    r = np.take_along_axis(w, np.broadcast_to(pick, w.shape[:2])[..., None], axis=-1)[..., 0]
+    return r >= np.uint32(threshold(p))
+
+
+def forward_backward(q, k, v, do, scale: float, p: float, seed: int, causal: bool = False,
+                     block_mask=None, mask_block: int = MASK_BLOCK):
+    """Forward and backward of attention with dropout (module docstring).
+
+    Returns a dict with O, LSE, dQ, dK, dV (fp64).
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, H, N, d = q.shape
+    keep = keep_matrix(N, N, causal, block_mask, mask_block)
+    inv_keep = 1.0 / (1.0 - p)
+    out = {name: np.empty_like(q) for name in ("O", "dQ", "dK", "dV")}
+    out["LSE"] = np.empty((B, H, N))
+    idx = np.arange(N)
+    for b in range(B):
+        for h in range(H):
+            bh = b * H + h
+            s = scale * (q[b, h] @ k[b, h].T)
+            s = np.where(keep, s, -np.inf)
+            pr, _, lse = _softmax_rows(s)
+            m = keep_mask(bh, idx, idx, p, seed) * inv_keep
+            o = (pr * m) @ v[b, h]
+            dv = (pr * m).T @ do[b, h]
+            dp = (do[b, h] @ v[b, h].T) * m
+            dvec = (do[b, h] * o).sum(axis=1)
+            ds = pr * (dp - dvec[:, None])
+            out["O"][b, h], out["LSE"][b, h] = o, lse
+            out["dQ"][b, h] = scale * (ds @ k[b, h])
+            out["dK"][b, h] = scale * (ds.T @ q[b, h])
+            out["dV"][b, h] = dv
+    return out
