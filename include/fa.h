@@ -61,7 +61,7 @@ typedef enum {
   FA_ERR_ALIGN = 5,      /* a tensor pointer is misaligned */
   FA_ERR_WORKSPACE = 6,  /* workspace NULL, misaligned or too small */
   FA_ERR_LAUNCH = 7,     /* the HIP runtime refused a kernel launch */
-  FA_ERR_ARG = 8,        /* scale not finite or negative */
+  FA_ERR_ARG = 8,        /* scale not finite or negative, or dropout_p outside [0, 1) */
   FA_ERR_ALIAS = 9       /* an output overlaps an input or another output */
 } fa_status;
 
@@ -152,6 +152,34 @@ fa_status fa_bwd_dq(const void* Q, const void* K, const void* V, const void* dO,
                     const float* LSE, void* dQ, int B, int H, int N, int d, float scale,
                     int causal, const unsigned char* block_mask, fa_dtype dtype,
                     const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_fwd_dropout / fa_bwd_dropout -- fa_fwd and fa_bwd with dropout on the
+ * attention probabilities, fused into the same kernels (the FlashAttention
+ * reading guide, xyznot.com/tr/paper/2205.14135, "Temel fikirler", lists
+ * dropout among the operations fused with the matrix products, masking and
+ * softmax).  With keep mask Z and M = Z / (1 - dropout_p):
+ *   O = (P * M) V;  LSE is that of the undropped P (unchanged by dropout);
+ *   dV = (P * M)^T dO,  dP = (dO V^T) * M,  D_i = sum_k dO_ik O_ik,
+ *   dS = P * (dP - D 1^T),  dQ = scale * dS K,  dK = scale * dS^T Q.
+ * Z is never stored: both calls regenerate it.  Element (i, j) (query i,
+ * key j) of head bh = b*H + h is kept iff word (j mod 4) of Philox4x32 with
+ * 10 rounds (Salmon, Moraes, Dror, Shaw, SC 2011) on counter
+ * (j / 4, i, bh, 0) with key (seed mod 2^32, seed / 2^32) is
+ * >= floor(dropout_p * 2^32).  fa_bwd_dropout must get the dropout_p and
+ * seed that fa_fwd_dropout got (and its O and LSE).  Other arguments as for
+ * fa_fwd / fa_bwd; dropout_p must lie in [0, 1) (else FA_ERR_ARG).
+ */
+fa_status fa_fwd_dropout(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                         int B, int H, int N, int d, float scale, int causal,
+                         const unsigned char* block_mask, float dropout_p,
+                         unsigned long long seed, fa_dtype dtype, void* stream);
+fa_status fa_bwd_dropout(const void* Q, const void* K, const void* V, const void* O,
+                         const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                         int B, int H, int N, int d, float scale, int causal,
+                         const unsigned char* block_mask, float dropout_p,
+                         unsigned long long seed, fa_dtype dtype, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char* fa_status_str(fa_status s);

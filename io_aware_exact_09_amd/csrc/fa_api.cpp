@@ -95,11 +95,53 @@ fa::BwdArgs bwd_args(const Shape& s, float scale, int causal, const unsigned cha
     if (st_ != FA_OK) return st_;    \
   } while (0)
 
+// Dropout probability p in [0, 1) and seed -> kernel parameters.
+fa_status dropout_params(float p, unsigned long long seed, fa::Dropout* out) {
+  if (!std::isfinite(p) || p < 0.f || p >= 1.f) return FA_ERR_ARG;
+  const double t = std::floor((double)p * 4294967296.0);
+  out->on = true;
+  out->key0 = (uint32_t)(seed & 0xFFFFFFFFull);
+  out->key1 = (uint32_t)(seed >> 32);
+  out->thresh = t >= 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
+  out->inv_keep = (float)(1.0 / (1.0 - (double)p));
+  return FA_OK;
+}
+
+fa_status fwd_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
+                   int H, int N, int d, float scale, int causal, const unsigned char* block_mask,
+                   fa_dtype dtype, const fa::Dropout& drop, void* stream);
+
+fa_status bwd_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                   const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int N, int d,
+                   float scale, int causal, const unsigned char* block_mask, fa_dtype dtype,
+                   void* workspace, size_t workspace_bytes, const fa::Dropout& drop,
+                   void* stream);
+
 }  // namespace
 
 FA_EXPORT fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
                            int B, int H, int N, int d, float scale, int causal,
                            const unsigned char* block_mask, fa_dtype dtype, void* stream) {
+  return fwd_impl(Q, K, V, O, LSE, B, H, N, d, scale, causal, block_mask, dtype, fa::Dropout{},
+                  stream);
+}
+
+FA_EXPORT fa_status fa_fwd_dropout(const void* Q, const void* K, const void* V, void* O,
+                                   float* LSE, int B, int H, int N, int d, float scale,
+                                   int causal, const unsigned char* block_mask, float dropout_p,
+                                   unsigned long long seed, fa_dtype dtype, void* stream) {
+  fa::Dropout drop;
+  FA_TRY(check_buffers({{Q, 0, 0}, {K, 0, 0}, {V, 0, 0}}, {{O, 0, 0}, {LSE, 0, 0}}));
+  FA_TRY(check_shape(Shape{B, H, N, d, dtype}, scale));
+  FA_TRY(dropout_params(dropout_p, seed, &drop));
+  return fwd_impl(Q, K, V, O, LSE, B, H, N, d, scale, causal, block_mask, dtype, drop, stream);
+}
+
+namespace {
+
+fa_status fwd_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
+                   int H, int N, int d, float scale, int causal, const unsigned char* block_mask,
+                   fa_dtype dtype, const fa::Dropout& drop, void* stream) {
   FA_TRY(check_buffers({{Q, 0, 0}, {K, 0, 0}, {V, 0, 0}}, {{O, 0, 0}, {LSE, 0, 0}}));
   const Shape s{B, H, N, d, dtype};
   FA_TRY(check_shape(s, scale));
@@ -115,9 +157,12 @@ FA_EXPORT fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O,
   a.scale = scale;
   a.causal = causal != 0;
   a.bf16 = dtype == FA_BF16;
+  a.drop = drop;
   a.stream = static_cast<hipStream_t>(stream);
   return fa::launch_fwd(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
+
+}  // namespace
 
 FA_EXPORT size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   const Shape s{B, H, N, d, FA_BF16};
@@ -183,6 +228,32 @@ FA_EXPORT fa_status fa_bwd(const void* Q, const void* K, const void* V, const vo
                            int B, int H, int N, int d, float scale, int causal,
                            const unsigned char* block_mask, fa_dtype dtype, void* workspace,
                            size_t workspace_bytes, void* stream) {
+  return bwd_impl(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, N, d, scale, causal, block_mask, dtype,
+                  workspace, workspace_bytes, fa::Dropout{}, stream);
+}
+
+FA_EXPORT fa_status fa_bwd_dropout(const void* Q, const void* K, const void* V, const void* O,
+                                   const void* dO, const float* LSE, void* dQ, void* dK,
+                                   void* dV, int B, int H, int N, int d, float scale, int causal,
+                                   const unsigned char* block_mask, float dropout_p,
+                                   unsigned long long seed, fa_dtype dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  fa::Dropout drop;
+  FA_TRY(check_buffers({{Q, 0, 0}, {K, 0, 0}, {V, 0, 0}, {O, 0, 0}, {dO, 0, 0}, {LSE, 0, 0}},
+                       {{dQ, 0, 0}, {dK, 0, 0}, {dV, 0, 0}}));
+  FA_TRY(check_shape(Shape{B, H, N, d, dtype}, scale));
+  FA_TRY(dropout_params(dropout_p, seed, &drop));
+  return bwd_impl(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, N, d, scale, causal, block_mask, dtype,
+                  workspace, workspace_bytes, drop, stream);
+}
+
+namespace {
+
+fa_status bwd_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                   const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int N, int d,
+                   float scale, int causal, const unsigned char* block_mask, fa_dtype dtype,
+                   void* workspace, size_t workspace_bytes, const fa::Dropout& drop,
+                   void* stream) {
   FA_TRY(check_buffers({{Q, 0, 0}, {K, 0, 0}, {V, 0, 0}, {O, 0, 0}, {dO, 0, 0}, {LSE, 0, 0}},
                        {{dQ, 0, 0}, {dK, 0, 0}, {dV, 0, 0}}));
   const Shape s{B, H, N, d, dtype};
@@ -198,11 +269,14 @@ FA_EXPORT fa_status fa_bwd(const void* Q, const void* K, const void* V, const vo
   a.q = Q; a.k = K; a.v = V; a.o = O; a.dout = dO; a.lse = LSE;
   a.dq = dQ; a.dk = dK; a.dv = dV;
   a.delta = static_cast<float*>(workspace);
+  a.drop = drop;
   if (fa::launch_bwd_preprocess(a) != hipSuccess) return FA_ERR_LAUNCH;
   if (fa::launch_bwd_dkdv(a) != hipSuccess) return FA_ERR_LAUNCH;
   if (fa::launch_bwd_dq(a) != hipSuccess) return FA_ERR_LAUNCH;
   return FA_OK;
 }
+
+}  // namespace
 
 FA_EXPORT const char* fa_status_str(fa_status s) {
   switch (s) {
@@ -214,7 +288,7 @@ FA_EXPORT const char* fa_status_str(fa_status s) {
     case FA_ERR_ALIGN: return "misaligned tensor pointer (16 bytes; LSE 4 bytes)";
     case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case FA_ERR_LAUNCH: return "kernel launch failed";
-    case FA_ERR_ARG: return "scale must be finite and >= 0";
+    case FA_ERR_ARG: return "scale must be finite and >= 0; dropout probability in [0, 1)";
     case FA_ERR_ALIAS: return "an output overlaps an input or another output";
   }
   return "unknown status";

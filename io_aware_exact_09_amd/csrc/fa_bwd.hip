@@ -72,14 +72,14 @@ struct DkdvCfg {
   static constexpr int SQ = 2 * BQ;                      // query rows per staged tile
 };
 
-template <typename T, int D, bool CAUSAL, bool MASKED>
+template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                    const T* __restrict__ dO, const float* __restrict__ LSE,
                    const float* __restrict__ delta, T* __restrict__ dK, T* __restrict__ dV,
                    const uint8_t* __restrict__ mask, int BH, int N, int T_tiles, float c,
-                   float scale) {
+                   float scale, DropParams drp) {
   using E = Elem<T>;
   using frag = typename E::frag;
   using Cfg = DkdvCfg<T>;
@@ -210,8 +210,20 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
             const int r = 4 * a + x;
             float p = __builtin_amdgcn_exp2f(fmaf(sv[r], c, -lv[x]));
             if (MASKED_TILE && krow > q0 + qi + x) p = 0.f;
-            sv[r] = p;
-            dpv[r] = p * (dpv[r] - dv[x]);
+            if constexpr (DROP) {
+              // dV takes the dropped probabilities (its 1/(1-p) is applied at
+              // the end); dS = P (dP M - D) with M = Z / (1-p).
+              const Philox4 z = philox4x32_10((uint32_t)krow >> 2, (uint32_t)(q0 + qi + x),
+                                              (uint32_t)bh, 0u, drp.key0, drp.key1);
+              const uint32_t word = (krow & 2) ? ((krow & 1) ? z.w[3] : z.w[2])
+                                               : ((krow & 1) ? z.w[1] : z.w[0]);
+              const bool keep = word >= drp.thresh;
+              sv[r] = keep ? p : 0.f;
+              dpv[r] = p * (keep ? fmaf(dpv[r], drp.inv_keep, -dv[x]) : -dv[x]);
+            } else {
+              sv[r] = p;
+              dpv[r] = p * (dpv[r] - dv[x]);
+            }
           }
         }
       };
@@ -373,8 +385,9 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int d0 = 32 * b + 8 * a + 4 * g;
-        E::store4(dVr + d0, dvacc[b][4 * a], dvacc[b][4 * a + 1], dvacc[b][4 * a + 2],
-                  dvacc[b][4 * a + 3]);
+        const float vs = DROP ? drp.inv_keep : 1.0f;
+        E::store4(dVr + d0, dvacc[b][4 * a] * vs, dvacc[b][4 * a + 1] * vs,
+                  dvacc[b][4 * a + 2] * vs, dvacc[b][4 * a + 3] * vs);
         E::store4(dKr + d0, dkacc[b][4 * a] * scale, dkacc[b][4 * a + 1] * scale,
                   dkacc[b][4 * a + 2] * scale, dkacc[b][4 * a + 3] * scale);
       }
@@ -395,14 +408,14 @@ struct DqCfg {
   static constexpr int BC = sizeof(T) == 2 ? 64 : 32;
 };
 
-template <typename T, int D, bool CAUSAL, bool MASKED>
+template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(Occupancy<T, D>::dq, Occupancy<T, D>::dq)))
 fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                  const T* __restrict__ dO, const float* __restrict__ LSE,
                  const float* __restrict__ delta, T* __restrict__ dQ,
                  const uint8_t* __restrict__ mask, int BH, int N, int T_tiles, float c,
-                 float scale) {
+                 float scale, DropParams drp) {
   using E = Elem<T>;
   using frag = typename E::frag;
   using Cfg = DqCfg<T>;
@@ -511,11 +524,28 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
       }
       // Register r holds key kv0 + 4g + 32h + 8(r/4) + r%4.
       const int lim = (CAUSAL ? min(N, qrow + 1) : N) - kv0 - 4 * g - 32 * h;
+      if constexpr (DROP) {
+        // dS = P (dP M - D), M = Z / (1-p); registers 4a..4a+3 are keys
+        // kv0 + 32h + 8a + 4g + x, one Philox call per group of four.
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
-        if (MASKED_TILE && 8 * (r >> 2) + (r & 3) >= lim) p = 0.f;
-        dp[r] = p * (dp[r] - dval);
+        for (int a = 0; a < 4; ++a) {
+          const Philox4 z = philox4x32_10((uint32_t)((kv0 + 32 * h + 8 * a) >> 2) + g,
+                                          (uint32_t)qrow, (uint32_t)bh, 0u, drp.key0, drp.key1);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const int r = 4 * a + x;
+            float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
+            if (MASKED_TILE && 8 * a + x >= lim) p = 0.f;
+            dp[r] = p * (z.w[x] >= drp.thresh ? fmaf(dp[r], drp.inv_keep, -dval) : -dval);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
+          if (MASKED_TILE && 8 * (r >> 2) + (r & 3) >= lim) p = 0.f;
+          dp[r] = p * (dp[r] - dval);
+        }
       }
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -597,24 +627,37 @@ static hipError_t launch_pre_t(const BwdArgs& a) {
   return hipGetLastError();
 }
 
+static DropParams drop_params(const BwdArgs& a) {
+  return DropParams{a.drop.key0, a.drop.key1, a.drop.thresh, a.drop.inv_keep};
+}
+
 template <typename T, int D, bool CAUSAL, bool MASKED>
 static hipError_t launch_dkdv_t(const BwdArgs& a) {
   const int nkb = (a.N + DkdvCfg<T>::BK - 1) / DkdvCfg<T>::BK;
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, CAUSAL, MASKED>), dim3(nkb * a.BH),
-                     dim3(kThreads), 0, a.stream, static_cast<const T*>(a.q),
-                     static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-                     static_cast<const T*>(a.dout), a.lse, a.delta, static_cast<T*>(a.dk),
-                     static_cast<T*>(a.dv), a.mask, a.BH, a.N, a.T, score_coef(a.scale), a.scale);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(nkb * a.BH), dim3(kThreads), 0, a.stream,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
+                       static_cast<T*>(a.dk), static_cast<T*>(a.dv), a.mask, a.BH, a.N, a.T,
+                       score_coef(a.scale), a.scale, drop_params(a));
+  };
+  if (a.drop.on) go(fa_bwd_dkdv_kernel<T, D, CAUSAL, MASKED, true>);
+  else go(fa_bwd_dkdv_kernel<T, D, CAUSAL, MASKED, false>);
   return hipGetLastError();
 }
 
 template <typename T, int D, bool CAUSAL, bool MASKED>
 static hipError_t launch_dq_t(const BwdArgs& a) {
   const int nqb = (a.N + DqCfg<T>::BR - 1) / DqCfg<T>::BR;
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, CAUSAL, MASKED>), dim3(nqb * a.BH), dim3(kThreads),
-                     0, a.stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                     static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
-                     static_cast<T*>(a.dq), a.mask, a.BH, a.N, a.T, score_coef(a.scale), a.scale);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(nqb * a.BH), dim3(kThreads), 0, a.stream,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
+                       static_cast<T*>(a.dq), a.mask, a.BH, a.N, a.T, score_coef(a.scale),
+                       a.scale, drop_params(a));
+  };
+  if (a.drop.on) go(fa_bwd_dq_kernel<T, D, CAUSAL, MASKED, true>);
+  else go(fa_bwd_dq_kernel<T, D, CAUSAL, MASKED, false>);
   return hipGetLastError();
 }
 

@@ -79,6 +79,36 @@ __device__ __forceinline__ unsigned char* pick(int v, unsigned char* b0, unsigne
 template <int V> __device__ __forceinline__ constexpr IntTag<V ^ 1> other(IntTag<V>) { return {}; }
 __device__ __forceinline__ int other(int v) { return v ^ 1; }
 
+// Philox4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel random
+// numbers: as easy as 1, 2, 3", SC 2011), written from the paper's
+// definition: each round multiplies words 0 and 2 by the two round constants,
+// keeps the low halves as the new words 3 and 1 and XORs the high halves with
+// the other two words and the key into the new words 0 and 2; the key
+// advances by the two Weyl constants between rounds.  A counter-based
+// generator: the dropout keep mask is recomputed wherever it is needed
+// instead of being stored.
+struct Philox4 { uint32_t w[4]; };
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                 uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+  }
+  return Philox4{{c0, c1, c2, c3}};
+}
+
+// Dropout parameters as the kernels receive them (unused unless the kernel
+// is instantiated with dropout).
+struct DropParams {
+  uint32_t key0, key1, thresh;
+  float inv_keep;
+};
+
 // Value of lane l ^ 32 exchanged without a trip through LDS:
 // v_permlane32_swap_b32 swaps the upper 32 lanes of its first register with
 // the lower 32 lanes of its second, so with both holding x the pair becomes

@@ -37,12 +37,12 @@ struct FwdCfg {
   static constexpr int BC = sizeof(T) == 2 ? 64 : 32;     // keys per tile
 };
 
-template <typename T, int D, bool CAUSAL, bool MASKED>
+template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(Occupancy<T, D>::fwd, Occupancy<T, D>::fwd)))
 fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
               T* __restrict__ O, float* __restrict__ LSE, const uint8_t* __restrict__ mask,
-              int BH, int N, int T_tiles, float c /* scale*log2e, > 0 */) {
+              int BH, int N, int T_tiles, float c /* scale*log2e, > 0 */, DropParams dp) {
   using E = Elem<T>;
   using frag = typename E::frag;
   using Cfg = FwdCfg<T>;
@@ -181,6 +181,23 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
 #pragma unroll
     for (int h = 0; h < NH; ++h) l_run += (psum[h][0] + psum[h][1]) + (psum[h][2] + psum[h][3]);
 
+    // ---- dropout: zero the dropped probabilities (the row sum above keeps
+    // them: softmax statistics are those of the undropped P; the 1/(1-p) of
+    // the kept ones is applied to O at the end).  Registers 4a..4a+3 of half h
+    // are keys kv0 + 32h + 8a + 4g + x, one Philox call per group of four.
+    if constexpr (DROP) {
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const Philox4 z = philox4x32_10((uint32_t)((kv0 + 32 * h + 8 * a) >> 2) + g,
+                                          (uint32_t)qrow, (uint32_t)bh, 0u, dp.key0, dp.key1);
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            if (z.w[x] < dp.thresh) s[h][4 * a + x] = 0.f;
+        }
+    }
+
     // ---- O^T += V_j^T P^T ----------------------------------------------------
     frag pf[NH][2];
 #pragma unroll
@@ -230,7 +247,7 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
 
   // ---- epilogue ----------------------------------------------------------------
   const float l_tot = sum_xor32(l_run);
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  const float inv = l_tot > 0.f ? (DROP ? dp.inv_keep : 1.0f) / l_tot : 0.f;
   if (qrow < N) {
     T* Orow = O + head + (size_t)qrow * D;
 #pragma unroll
@@ -249,10 +266,17 @@ template <typename T, int D, bool CAUSAL, bool MASKED>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
   const int nqb = (a.N + FwdCfg<T>::BR - 1) / FwdCfg<T>::BR;
   const dim3 grid(nqb * a.BH), block(kThreads);
-  hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, MASKED>), grid, block, 0, a.stream,
-                     static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                     static_cast<const T*>(a.v), static_cast<T*>(a.o), a.lse, a.mask, a.BH,
-                     a.N, a.T, score_coef(a.scale));
+  const DropParams dp{a.drop.key0, a.drop.key1, a.drop.thresh, a.drop.inv_keep};
+  if (a.drop.on)
+    hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, MASKED, true>), grid, block, 0, a.stream,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), static_cast<T*>(a.o), a.lse, a.mask, a.BH,
+                       a.N, a.T, score_coef(a.scale), dp);
+  else
+    hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, MASKED, false>), grid, block, 0, a.stream,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), static_cast<T*>(a.o), a.lse, a.mask, a.BH,
+                       a.N, a.T, score_coef(a.scale), dp);
   return hipGetLastError();
 }
 
@@ -498,7 +522,7 @@ static hipError_t launch_fwd_d(const FwdArgs& a) {
 hipError_t launch_fwd(const FwdArgs& a) {
   // d = 128 without a block mask: the ping-pong kernel.  (At d = 64 the
   // four-wave kernel runs three waves per SIMD and measured faster.)
-  if (a.bf16 && !a.mask && a.d == 128)
+  if (a.bf16 && !a.mask && a.d == 128 && !a.drop.on)
     return a.causal ? launch_fwd_pp<__bf16, 128, true>(a) : launch_fwd_pp<__bf16, 128, false>(a);
   if (a.bf16) return a.d == 64 ? launch_fwd_d<__bf16, 64>(a) : launch_fwd_d<__bf16, 128>(a);
   return a.d == 64 ? launch_fwd_d<float, 64>(a) : launch_fwd_d<float, 128>(a);

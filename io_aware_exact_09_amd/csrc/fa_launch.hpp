@@ -7,6 +7,17 @@
 
 namespace fa {
 
+// Dropout on the attention probabilities (see philox4x32_10 in
+// fa_common.hpp): element (i, j) of head bh is kept iff word j % 4 of
+// Philox4x32-10(counter (j / 4, i, bh, 0), key (key0, key1)) >= thresh;
+// kept probabilities are scaled by inv_keep = 1 / (1 - p).
+struct Dropout {
+  bool on = false;
+  uint32_t key0 = 0, key1 = 0;
+  uint32_t thresh = 0;
+  float inv_keep = 1.f;
+};
+
 struct FwdArgs {
   const void* q; const void* k; const void* v;
   void* o; float* lse;
@@ -14,6 +25,7 @@ struct FwdArgs {
   int BH, N, d, T;         // T = ceil(N / 128) (mask side)
   float scale;
   bool causal, bf16;
+  Dropout drop;
   hipStream_t stream;
 };
 
@@ -26,6 +38,7 @@ struct BwdArgs {
   int BH, N, d, T;
   float scale;
   bool causal, bf16;
+  Dropout drop;
   hipStream_t stream;
 };
 

@@ -70,6 +70,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa_bwd_dkdv.restype = i
         lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp]
         lib.fa_bwd_dq.restype = i
+        u64 = ctypes.c_ulonglong
+        lib.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, f, u64, i, vp]
+        lib.fa_fwd_dropout.restype = i
+        lib.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp,
+                                       f, u64, i, vp, sz, vp]
+        lib.fa_bwd_dropout.restype = i
         lib.fa_status_str.argtypes = [i]
         lib.fa_status_str.restype = ctypes.c_char_p
         _lib = lib
@@ -163,6 +169,38 @@ def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = False,
                     _ptr(block_mask), _dtype_code(q), _ptr(workspace), wbytes,
                     _stream(stream))
     _check(st, "fa_bwd")
+
+
+def fa_fwd_dropout(q, k, v, o, lse, scale: float, dropout_p: float, seed: int,
+                   causal: bool = False, block_mask=None, stream=None) -> None:
+    """fa_fwd with dropout on the probabilities (keep probability 1 - p; the
+    keep mask is regenerated from ``seed`` by fa_bwd_dropout)."""
+    lib = load_library()
+    _check_tensors(q, dict(q=q, k=k, v=v, o=o, lse=lse))
+    _mask_ok(q, block_mask)
+    B, H, N, d = q.shape
+    st = lib.fa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                            float(scale), int(bool(causal)), _ptr(block_mask), float(dropout_p),
+                            int(seed) & (2 ** 64 - 1), _dtype_code(q), _stream(stream))
+    _check(st, "fa_fwd_dropout")
+
+
+def fa_bwd_dropout(q, k, v, o, do, lse, dq, dk, dv, scale: float, dropout_p: float, seed: int,
+                   causal: bool = False, block_mask=None, workspace=None, stream=None) -> None:
+    """fa_bwd for outputs of fa_fwd_dropout (same dropout_p and seed)."""
+    lib = load_library()
+    _check_tensors(q, dict(q=q, k=k, v=v, o=o, do=do, lse=lse, dq=dq, dk=dk, dv=dv))
+    _mask_ok(q, block_mask)
+    B, H, N, d = q.shape
+    if workspace is None:
+        workspace = torch.empty(max(fa_bwd_workspace_bytes(B, H, N, d), 1), dtype=torch.uint8,
+                                device=q.device)
+    st = lib.fa_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                            _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
+                            _ptr(block_mask), float(dropout_p), int(seed) & (2 ** 64 - 1),
+                            _dtype_code(q), _ptr(workspace), _nbytes(workspace),
+                            _stream(stream))
+    _check(st, "fa_bwd_dropout")
 
 
 def _mask_ok(q, block_mask):

@@ -30,7 +30,8 @@ def lib():
 def test_header_symbols_are_exported(lib):
     names = fa.header_functions()
     assert set(names) == {"fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
-                          "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq"}
+                          "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
+                          "fa_fwd_dropout", "fa_bwd_dropout"}
     out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -94,6 +95,44 @@ def test_fwd_validation(lib, kw, code):
 ])
 def test_bwd_validation(lib, kw, code):
     assert bwd(lib, **kw) == code
+
+
+def fwd_drop(lib, pdrop=0.1, seed=7, **kw):
+    a = dict(q=p(0), k=p(1), v=p(2), o=p(3), lse=p(4), B=1, H=2, N=128, d=64, scale=0.125,
+             causal=0, mask=None, dtype=BF16)
+    a.update(kw)
+    return lib.fa_fwd_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"],
+                              a["d"], a["scale"], a["causal"], a["mask"], pdrop, seed,
+                              a["dtype"], None)
+
+
+def bwd_drop(lib, pdrop=0.1, seed=7, **kw):
+    a = dict(q=p(0), k=p(1), v=p(2), o=p(3), do=p(4), lse=p(5), dq=p(6), dk=p(7), dv=p(8),
+             B=1, H=2, N=128, d=64, scale=0.125, causal=0, mask=None, dtype=BF16, ws=p(9),
+             wsb=1 << 20)
+    a.update(kw)
+    return lib.fa_bwd_dropout(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"],
+                              a["dk"], a["dv"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                              a["causal"], a["mask"], pdrop, seed, a["dtype"], a["ws"], a["wsb"],
+                              None)
+
+
+@pytest.mark.parametrize("pdrop", [-0.1, 1.0, 1.5, float("nan"), float("inf")])
+def test_dropout_probability_validation(lib, pdrop):
+    assert fwd_drop(lib, pdrop=pdrop) == 8
+    assert bwd_drop(lib, pdrop=pdrop) == 8
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(N=0), 2), (dict(d=96), 3), (dict(dtype=7), 4),
+    (dict(q=p(0, 8)), 5), (dict(o=p(0, 64)), 9),
+])
+def test_dropout_entry_points_check_like_the_plain_ones(lib, kw, code):
+    assert fwd_drop(lib, **kw) == code
+    bkw = {k2: v2 for k2, v2 in kw.items() if k2 != "o"}
+    if kw.get("o") is not None and "o" in kw:
+        bkw["dq"] = p(0, 64)
+    assert bwd_drop(lib, **bkw) == code
 
 
 def test_status_codes_match_header():
