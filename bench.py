@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the CPU oracle sample")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="time fa_fwd_dropout + fa_bwd_dropout with this dropout probability "
+                         "(the headline line is the dropout-free step)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain device copy of FA_COPY_PROBE_BYTES (512 MiB) first, "
                          "to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -142,9 +145,18 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    phases = ["fwd", "pre", "dkdv", "dq"]
+    drop = args.dropout
+    phases = ["fwd", "bwd"] if drop > 0 else ["fwd", "pre", "dkdv", "dq"]
 
     def step(ev=None):
+        if drop > 0:
+            # the backward's three kernels run inside one entry point here
+            if ev: ev[0].record()
+            fa.fa_fwd_dropout(q, k, v, o, lse, sc, drop, 1234, cz, mask)
+            if ev: ev[1].record()
+            fa.fa_bwd_dropout(q, k, v, o, do, lse, dq, dk, dv, sc, drop, 1234, cz, mask, ws)
+            if ev: ev[2].record()
+            return
         if ev: ev[0].record()
         fa.fa_fwd(q, k, v, o, lse, sc, cz, mask)
         if ev: ev[1].record()
@@ -159,7 +171,8 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    nev = len(phases) + 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -168,8 +181,8 @@ def main():
     wall = time.perf_counter() - t0
 
     per = {p: [e[i].elapsed_time(e[i + 1]) for e in evs] for i, p in enumerate(phases)}
-    steps_ms = [e[0].elapsed_time(e[4]) for e in evs]
-    span_ms = evs[0][0].elapsed_time(evs[-1][4])
+    steps_ms = [e[0].elapsed_time(e[nev - 1]) for e in evs]
+    span_ms = evs[0][0].elapsed_time(evs[-1][nev - 1])
     ms_step = span_ms / args.steps
     fl = accounting.flops(w.B, w.H, w.N, w.d, w.causal, x["mask"])
     elem = 2 if w.dtype == "bf16" else 4
@@ -179,13 +192,14 @@ def main():
     value = total / (ms_step * 1e-3) / 1e12
 
     avg = {p: statistics.mean(per[p]) for p in phases}
-    kflops = {"fwd": fl["fwd_kernel"], "dkdv": fl["dkdv_kernel"], "dq": fl["dq_kernel"]}
+    kflops = {"fwd": fl["fwd_kernel"], "dkdv": fl["dkdv_kernel"], "dq": fl["dq_kernel"],
+              "bwd": fl["bwd"]}
     # The library runs bf16, d = 128 without a block mask on the ping-pong
     # forward kernel, everything else on the four-wave one.
     fwd_name = ("fa_fwd_pp_kernel" if w.dtype == "bf16" and w.d == 128 and w.mask_density is None
-                else "fa_fwd_kernel")
+                and drop == 0 else "fa_fwd_kernel")
     names = {"fwd": fwd_name, "pre": "fa_bwd_delta_kernel", "dkdv": "fa_bwd_dkdv_kernel",
-             "dq": "fa_bwd_dq_kernel"}
+             "dq": "fa_bwd_dq_kernel", "bwd": "fa_bwd_dropout (three kernels)"}
     dom = max(phases, key=lambda p: avg[p])
     if dom == "pre":
         ach = hb["pre_kernel"] / (avg[dom] * 1e-3) / 1e9
@@ -209,7 +223,7 @@ def main():
         kernels[names[p]] = entry
 
     fwd_ms = avg["fwd"]
-    bwd_ms = avg["pre"] + avg["dkdv"] + avg["dq"]
+    bwd_ms = avg["bwd"] if drop > 0 else avg["pre"] + avg["dkdv"] + avg["dq"]
     s = sorted(steps_ms)
     n = len(s)
     mean = statistics.mean(s)
@@ -237,6 +251,7 @@ def main():
         "data": "synthetic (seeded iid normal Q, K, V, dO)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "block_sparse": x["mask"] is not None,
+                   "dropout": drop,
                    "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)"},
         "pct_of_peak": 100.0 * value / peak,
         "fwd_tflops": fl["fwd"] / (fwd_ms * 1e-3) / 1e12,
