@@ -77,6 +77,67 @@ WORKLOADS = {
 }
 
 
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """A few new query rows per sequence against a key/value cache, with
+    Hkv cache heads shared by groups of Hq / Hkv query heads."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nkv: int
+    d: int
+    dtype: str
+    causal: bool
+    lengths: str = "full"     # "full": every sequence Nkv long; "uniform": U{1..Nkv}
+    sigma: float = 1.0
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def with_shape(self, **kw) -> "DecodeWorkload":
+        return replace(self, **kw)
+
+
+# Decode shapes from the week-13 page's decode discussion: a batch of 64
+# requests at an 8K context, 32 query heads over 8 cache heads (the Llama-3-8B
+# grouping it quotes), d = 128; "spec" checks 4 draft tokens per request at
+# once (speculative decoding with gamma = 3), causal among themselves.
+# Recipe: rng = default_rng(seed); Q [B, Hq, Nq, d], then K, V [B, Hkv, Nkv, d]
+# as standard_normal(float32) * sigma; then the lengths (``uniform``:
+# rng.integers(1, Nkv + 1, B)); then bf16 rounding.
+DECODE_WORKLOADS = {
+    "decode": DecodeWorkload("decode", 64, 32, 8, 1, 8192, 128, "bf16", False, seed=1101),
+    "decode_mix": DecodeWorkload("decode_mix", 64, 32, 8, 1, 8192, 128, "bf16", False,
+                                 lengths="uniform", seed=1102),
+    "decode_spec": DecodeWorkload("decode_spec", 64, 32, 8, 4, 8192, 128, "bf16", True,
+                                  lengths="uniform", seed=1103),
+}
+
+
+def make_decode_inputs(w: DecodeWorkload, seed: Optional[int] = None) -> dict:
+    """Draw the inputs of decode workload ``w``: dict(q [B,Hq,Nq,d],
+    k, v [B,Hkv,Nkv,d] float32 holding the storage-type values, seqlens int32
+    [B], scale, causal, dtype)."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    sig = np.float32(w.sigma)
+    q = rng.standard_normal((w.B, w.Hq, w.Nq, w.d), dtype=np.float32) * sig
+    k = rng.standard_normal((w.B, w.Hkv, w.Nkv, w.d), dtype=np.float32) * sig
+    v = rng.standard_normal((w.B, w.Hkv, w.Nkv, w.d), dtype=np.float32) * sig
+    if w.lengths == "full":
+        lens = np.full(w.B, w.Nkv, dtype=np.int32)
+    elif w.lengths == "uniform":
+        lens = rng.integers(1, w.Nkv + 1, size=w.B).astype(np.int32)
+    else:
+        raise ValueError(f"unknown length mix {w.lengths!r}")
+    if w.dtype == "bf16":
+        q, k, v = (bf16_round(t) for t in (q, k, v))
+    return dict(q=q, k=k, v=v, seqlens=lens, scale=w.scale, causal=w.causal, dtype=w.dtype)
+
+
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even); returns float32
     holding exactly representable bf16 values.  Inputs must be finite."""

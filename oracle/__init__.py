@@ -32,3 +32,4 @@ from .online import (  # noqa: F401
     tiled_forward_rescaled,
     tiled_forward_deferred,
 )
+from . import decode  # noqa: F401
