@@ -124,6 +124,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.workload in W.DECODE_WORKLOADS:
+        return bench_decode(args)
     w = W.WORKLOADS[args.workload]
     x = W.make_inputs(w)
     dev = torch.device("cuda:0")
@@ -265,6 +267,120 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "peak_tflops": peak,
+    }
+    print(json.dumps(out))
+
+
+def cpu_baseline_decode(w, x, budget_s):
+    """Time the fp64 decode oracle on whole sequences (all heads) for about
+    budget_s seconds."""
+    import oracle
+    from io_aware_exact_09_amd import accounting
+    try:
+        import threadpoolctl
+        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()),
+                      default=os.cpu_count())
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    done = []
+    t0 = time.perf_counter()
+    for b in range(w.B):
+        sl = slice(b, b + 1)
+        oracle.decode.decode_forward(x["q"][sl], x["k"][sl], x["v"][sl], w.scale,
+                                     x["seqlens"][sl], w.causal)
+        done.append(b)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    elem = 2 if w.dtype == "bf16" else 4
+    by = accounting.decode_bytes(len(done), w.Hq, w.Hkv, w.Nq, w.d, elem, x["seqlens"][done])
+    return {
+        "value": by["total"] / el / 1e9,
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(done)} of {w.B} sequences (all heads, fp64 NumPy), {el:.1f} s",
+    }
+
+
+def bench_decode(args):
+    """Split-KV decode: one step is one fa_decode call (its chunk kernel and,
+    with several chunks, the merge kernel) over the whole batch."""
+    import torch
+    from io_aware_exact_09_amd import accounting, fa
+    from io_aware_exact_09_amd import workloads as W
+
+    w = W.DECODE_WORKLOADS[args.workload]
+    x = W.make_decode_inputs(w)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x[n]).to(dev).to(tdt).contiguous() for n in ("q", "k", "v"))
+    sl = torch.from_numpy(x["seqlens"]).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    S = fa.fa_decode_num_splits(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.d)
+    nws = fa.fa_decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.d)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+    if args.copy_probe:
+        n = int(os.environ.get("FA_COPY_PROBE_BYTES", 512 << 20))
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def step():
+        fa.fa_decode(q, k, v, o, lse, w.scale, sl, w.causal, 0, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record()
+        step()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [e[0].elapsed_time(e[1]) for e in evs]
+    ms_step = evs[0][0].elapsed_time(evs[-1][1]) / args.steps
+    elem = 2 if w.dtype == "bf16" else 4
+    by = accounting.decode_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.d, elem, x["seqlens"])
+    value = by["total"] / (ms_step * 1e-3) / 1e9
+    avg = statistics.mean(per)
+    ach = by["total"] / (avg * 1e-3) / 1e9
+    name = "fa_decode_split_kernel" + (" + fa_decode_combine_kernel" if S > 1 else "")
+    roof = {"kernel": name, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+            "traffic": recorded_traffic(w.name, "fa_decode_split_kernel"),
+            "algorithmic_bytes_per_launch": by["total"], "avg_launch_ms": avg}
+    cpu = None if args.no_cpu else cpu_baseline_decode(w, x, args.cpu_seconds)
+    s = sorted(per)
+    out = {
+        "metric": "decode attention HBM GB/s (bf16, 1 MI355X) and % of 8 TB/s",
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded iid normal Q and key/value cache)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq,
+                   "Nkv": w.Nkv, "d": w.d, "causal": w.causal, "lengths": w.lengths,
+                   "cache_tokens": int(np.asarray(x["seqlens"]).sum()), "chunks": S,
+                   "parallelism": "none (1 GPU)"},
+        "pct_of_peak": 100.0 * value / HBM_PEAK_GBS,
+        "tflops": by["flops"] / (ms_step * 1e-3) / 1e12,
+        "step_ms_stats": {"mean": statistics.mean(s), "p50": s[len(s) // 2],
+                          "p95": s[min(len(s) - 1, int(0.95 * len(s)))]},
+        "wall_s_timed": wall,
+        "roofline": roof,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out))
 

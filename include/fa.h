@@ -61,7 +61,8 @@ typedef enum {
   FA_ERR_ALIGN = 5,      /* a tensor pointer is misaligned */
   FA_ERR_WORKSPACE = 6,  /* workspace NULL, misaligned or too small */
   FA_ERR_LAUNCH = 7,     /* the HIP runtime refused a kernel launch */
-  FA_ERR_ARG = 8,        /* scale not finite or negative, or dropout_p outside [0, 1) */
+  FA_ERR_ARG = 8,        /* scale not finite or negative, dropout_p outside [0, 1),
+                            or num_splits outside [0, 1024] */
   FA_ERR_ALIAS = 9       /* an output overlaps an input or another output */
 } fa_status;
 
@@ -180,6 +181,56 @@ fa_status fa_bwd_dropout(const void* Q, const void* K, const void* V, const void
                          const unsigned char* block_mask, float dropout_p,
                          unsigned long long seed, fa_dtype dtype, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/*
+ * fa_decode -- attention of a few new query rows against a key/value cache,
+ * with grouped key/value heads (inference decode; the week-13 page's note on
+ * decode attention and GQA, snula.amonoc.com/course/ru/week-13.html).
+ *
+ * For batch entry b, query head h (cache head kvh = h / (Hq / Hkv)) and new
+ * query row i:
+ *   O_bhi   = sum_j P_j V[b, kvh, j],  P_j = exp(s_j - LSE_bhi) over visible j,
+ *   LSE_bhi = ln sum_{visible j} exp(s_j),  s_j = scale * <Q_bhi, K[b, kvh, j]>,
+ * where key j is visible iff j < L_b and, with causal != 0, j <= L_b - Nq + i
+ * (the Nq new tokens are the last Nq positions of the sequence).  A row with
+ * no visible key gets O = 0 and LSE = -inf.  The keys of each (b, kvh) are
+ * cut into chunks handled by separate work-groups (each cache byte is read
+ * once and serves the Hq / Hkv query heads of its group); the chunks' partial
+ * (LSE, O) are merged with the two-part rule of [FA-guide] "Artımsal Softmax
+ * Takibi" by a second kernel.  Arithmetic as in fa_fwd.
+ *
+ *   Q        in : [B, Hq, Nq, d] dtype
+ *   K, V     in : [B, Hkv, Nkv, d] dtype (cache rows at or past L_b are never read)
+ *   seqlens  in : device int32[B] with L_b in [0, Nkv] (values outside are
+ *                 clamped to that range), or NULL: every L_b = Nkv
+ *   O        out: [B, Hq, Nq, d] dtype (overwritten)
+ *   LSE      out: [B, Hq, Nq] fp32 (overwritten)
+ *   num_splits    0: the library picks the number of key chunks; n >= 1: at
+ *                 most n chunks (n <= 1024)
+ *   workspace     scratch of at least fa_decode_workspace_bytes(...) bytes
+ *                 (0 when a single chunk is used: then workspace may be NULL),
+ *                 16-byte aligned, caller-owned, contents overwritten.
+ *
+ * Hq must be a multiple of Hkv (FA_ERR_SHAPE otherwise); B, Hq, Hkv, Nq,
+ * Nkv >= 1; Nkv * d and B * Hq * Nq * d must fit in int32; seqlens 4-byte
+ * aligned.  Other conventions as above.
+ */
+fa_status fa_decode(const void* Q, const void* K, const void* V, const int* seqlens, void* O,
+                    float* LSE, int B, int Hq, int Hkv, int Nq, int Nkv, int d, float scale,
+                    int causal, int num_splits, fa_dtype dtype, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
+ * fa_decode_num_splits -- the number of key chunks fa_decode uses for these
+ * sizes and num_splits (1: no merge kernel and no workspace); 0 for sizes
+ * fa_decode would reject.
+ * fa_decode_workspace_bytes -- the workspace fa_decode needs for them:
+ * (d + 1) * 4 bytes per query row and chunk when more than one chunk is used,
+ * else 0 (also 0 for rejected sizes).
+ */
+int fa_decode_num_splits(int B, int Hq, int Hkv, int Nq, int Nkv, int d, int num_splits);
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nkv, int d,
+                                 int num_splits);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char* fa_status_str(fa_status s);

@@ -49,3 +49,17 @@ def hbm_bytes(B: int, H: int, N: int, d: int, elem: int) -> dict:
         "dkdv_kernel": 4 * t + 2 * r + 2 * t,        # read Q K V dO LSE D, write dK dV
         "dq_kernel": 4 * t + 2 * r + t,              # read Q K V dO LSE D, write dQ
     }
+
+
+def decode_bytes(B: int, Hq: int, Hkv: int, Nq: int, d: int, elem: int, seqlens) -> dict:
+    """Minimal algorithmic HBM bytes of one decode call: the visible cache rows
+    of K and V read once (each cache head once, whatever the number of query
+    heads sharing it), Q read and O written once, LSE 4 bytes per row.  Also
+    the matrix FLOPs (4 d per query row and visible key; causal rows of the
+    Nq new tokens see slightly fewer keys, which is ignored)."""
+    kv_rows = int(np.asarray(seqlens, dtype=np.int64).sum()) * Hkv
+    rows = B * Hq * Nq
+    cache = 2 * kv_rows * d * elem
+    qo = 2 * rows * d * elem + 4 * rows
+    flops = 4 * d * Nq * (Hq // Hkv) * kv_rows
+    return {"cache": cache, "q_o_lse": qo, "total": cache + qo, "flops": flops}

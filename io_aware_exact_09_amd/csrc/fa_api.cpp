@@ -8,7 +8,10 @@
 #include <cstdint>
 #include <initializer_list>
 
+#include <algorithm>
+
 #include "../../include/fa.h"
+#include "fa_decode.hpp"
 #include "fa_launch.hpp"
 
 #define FA_EXPORT extern "C" __attribute__((visibility("default")))
@@ -278,17 +281,126 @@ fa_status bwd_impl(const void* Q, const void* K, const void* V, const void* O, c
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Decode
+// ---------------------------------------------------------------------------
+
+namespace fa {
+
+DecodePlan decode_plan(int B, int Hkv, int R, int Nkv, int num_splits) {
+  constexpr int kTile = 128;               // keys per tile (bf16 kernels)
+  constexpr int kMinChunk = 512;           // automatic chunks span at least 4 tiles
+  constexpr long long kMaxAuto = 128;
+  // About 8 work-groups per compute unit of the 256-CU MI355X, so chunks of
+  // sequences of different lengths balance over the device.
+  constexpr long long kTargetGroups = 2048;
+  const long long pairs = (long long)B * Hkv * ((R + 31) / 32);
+  const int tiles = (Nkv + kTile - 1) / kTile;
+  long long S = num_splits;
+  if (S <= 0) {
+    S = std::min(kMaxAuto, (kTargetGroups + pairs - 1) / pairs);
+    S = std::min<long long>(S, std::max(1, (Nkv + kMinChunk - 1) / kMinChunk));
+  }
+  S = std::max<long long>(1, std::min<long long>(S, tiles));
+  const int per = (int)((Nkv + S - 1) / S);
+  const int chunk = (per + kTile - 1) / kTile * kTile;
+  return DecodePlan{(Nkv + chunk - 1) / chunk, chunk};
+}
+
+}  // namespace fa
+
+namespace {
+
+struct DecShape {
+  int B, Hq, Hkv, Nq, Nkv, d;
+  fa_dtype dtype;
+  int R() const { return (Hq / Hkv) * Nq; }
+  uintptr_t elem() const { return dtype == FA_BF16 ? 2 : 4; }
+  uintptr_t q_bytes() const { return (uintptr_t)B * Hq * Nq * d * elem(); }
+  uintptr_t kv_bytes() const { return (uintptr_t)B * Hkv * Nkv * d * elem(); }
+  uintptr_t rows() const { return (uintptr_t)B * Hq * Nq; }
+};
+
+fa_status check_decode_shape(const DecShape& s, int num_splits) {
+  if (s.dtype != FA_BF16 && s.dtype != FA_FP32) return FA_ERR_DTYPE;
+  if (s.B < 1 || s.Hq < 1 || s.Hkv < 1 || s.Nq < 1 || s.Nkv < 1) return FA_ERR_SHAPE;
+  if (s.Hq % s.Hkv) return FA_ERR_SHAPE;
+  if (s.d != 64 && s.d != 128) return FA_ERR_HEAD_DIM;
+  const long long qe = (long long)s.B * s.Hq * s.Nq * s.d;
+  const long long pairs = (long long)s.B * s.Hkv;
+  const long long groups = pairs * ((s.R() + 31) / 32) * ((s.Nkv + 127) / 128);
+  if ((long long)s.Nkv * s.d > INT_MAX || qe > INT_MAX || groups > INT_MAX)
+    return FA_ERR_SHAPE;
+  if (num_splits < 0 || num_splits > 1024) return FA_ERR_ARG;
+  return FA_OK;
+}
+
+size_t decode_workspace(const DecShape& s, const fa::DecodePlan& p) {
+  return p.S > 1 ? (size_t)s.rows() * p.S * (s.d + 1) * 4 : 0;
+}
+
+}  // namespace
+
+FA_EXPORT int fa_decode_num_splits(int B, int Hq, int Hkv, int Nq, int Nkv, int d,
+                                   int num_splits) {
+  const DecShape s{B, Hq, Hkv, Nq, Nkv, d, FA_BF16};
+  if (check_decode_shape(s, num_splits) != FA_OK) return 0;
+  return fa::decode_plan(B, Hkv, s.R(), Nkv, num_splits).S;
+}
+
+FA_EXPORT size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nkv, int d,
+                                           int num_splits) {
+  const DecShape s{B, Hq, Hkv, Nq, Nkv, d, FA_BF16};
+  if (check_decode_shape(s, num_splits) != FA_OK) return 0;
+  return decode_workspace(s, fa::decode_plan(B, Hkv, s.R(), Nkv, num_splits));
+}
+
+FA_EXPORT fa_status fa_decode(const void* Q, const void* K, const void* V, const int* seqlens,
+                              void* O, float* LSE, int B, int Hq, int Hkv, int Nq, int Nkv,
+                              int d, float scale, int causal, int num_splits, fa_dtype dtype,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  FA_TRY(check_buffers({{Q, 0, 0}, {K, 0, 0}, {V, 0, 0}}, {{O, 0, 0}, {LSE, 0, 0}}));
+  const DecShape s{B, Hq, Hkv, Nq, Nkv, d, dtype};
+  FA_TRY(check_decode_shape(s, num_splits));
+  if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_ARG;
+  const fa::DecodePlan plan = fa::decode_plan(B, Hkv, s.R(), Nkv, num_splits);
+  const size_t need = decode_workspace(s, plan);
+  const Buf q{Q, s.q_bytes(), 16}, k{K, s.kv_bytes(), 16}, v{V, s.kv_bytes(), 16};
+  const Buf o{O, s.q_bytes(), 16}, l{LSE, s.rows() * 4, 4};
+  const Buf sl{seqlens, seqlens ? (uintptr_t)B * 4 : 0, 4};
+  const Buf ws{workspace, workspace_bytes, 16};
+  FA_TRY(check_layout({q, k, v, sl}, {o, l}, need ? &ws : nullptr, true, need));
+
+  fa::DecodeArgs a{};
+  a.q = Q; a.k = K; a.v = V;
+  a.seqlens = reinterpret_cast<const int32_t*>(seqlens);
+  a.o = O; a.lse = LSE;
+  a.opart = need ? static_cast<float*>(workspace) : nullptr;
+  a.lpart = need ? static_cast<float*>(workspace) + s.rows() * plan.S * d : nullptr;
+  a.pairs = B * Hkv;
+  a.Hkv = Hkv; a.Nq = Nq; a.R = s.R(); a.Nkv = Nkv; a.d = d;
+  a.S = plan.S; a.chunk = plan.chunk;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.bf16 = dtype == FA_BF16;
+  a.stream = static_cast<hipStream_t>(stream);
+  return fa::launch_decode(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 FA_EXPORT const char* fa_status_str(fa_status s) {
   switch (s) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "null pointer argument";
-    case FA_ERR_SHAPE: return "invalid shape (B, H, N must be >= 1 and sizes must fit int32)";
+    case FA_ERR_SHAPE:
+      return "invalid shape (sizes must be >= 1 and fit int32; Hq a multiple of Hkv)";
     case FA_ERR_HEAD_DIM: return "head dimension must be 64 or 128";
     case FA_ERR_DTYPE: return "unknown dtype";
     case FA_ERR_ALIGN: return "misaligned tensor pointer (16 bytes; LSE 4 bytes)";
     case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case FA_ERR_LAUNCH: return "kernel launch failed";
-    case FA_ERR_ARG: return "scale must be finite and >= 0; dropout probability in [0, 1)";
+    case FA_ERR_ARG:
+      return "scale must be finite and >= 0; dropout probability in [0, 1); num_splits in "
+             "[0, 1024]";
     case FA_ERR_ALIAS: return "an output overlaps an input or another output";
   }
   return "unknown status";

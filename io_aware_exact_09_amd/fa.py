@@ -76,6 +76,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp,
                                        f, u64, i, vp, sz, vp]
         lib.fa_bwd_dropout.restype = i
+        lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, sz,
+                                  vp]
+        lib.fa_decode.restype = i
+        lib.fa_decode_num_splits.argtypes = [i] * 7
+        lib.fa_decode_num_splits.restype = i
+        lib.fa_decode_workspace_bytes.argtypes = [i] * 7
+        lib.fa_decode_workspace_bytes.restype = sz
         lib.fa_status_str.argtypes = [i]
         lib.fa_status_str.restype = ctypes.c_char_p
         _lib = lib
@@ -250,7 +257,48 @@ def fa_bwd_dq(q, k, v, do, lse, dq, scale, causal=False, block_mask=None, worksp
     _check(st, "fa_bwd_dq")
 
 
+def fa_decode_num_splits(B, Hq, Hkv, Nq, Nkv, d, num_splits=0) -> int:
+    """Key chunks fa_decode uses for these sizes (0 for rejected sizes)."""
+    return int(load_library().fa_decode_num_splits(B, Hq, Hkv, Nq, Nkv, d, num_splits))
+
+
+def fa_decode_workspace_bytes(B, Hq, Hkv, Nq, Nkv, d, num_splits=0) -> int:
+    return int(load_library().fa_decode_workspace_bytes(B, Hq, Hkv, Nq, Nkv, d, num_splits))
+
+
+def fa_decode(q, k, v, o, lse, scale: float, seqlens=None, causal: bool = False,
+              num_splits: int = 0, workspace=None, stream=None) -> None:
+    """Enqueue decode attention: q, o [B,Hq,Nq,d]; k, v (the cache)
+    [B,Hkv,Nkv,d]; lse [B,Hq,Nq] fp32; seqlens None or an int32 device tensor
+    [B].  ``workspace`` is allocated here if None and needed."""
+    lib = load_library()
+    _check_tensors(q, dict(q=q, k=k, v=v, o=o, lse=lse))
+    B, Hq, Nq, d = q.shape
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    if seqlens is not None:
+        _check_tensors(q, dict(seqlens=seqlens))
+        if seqlens.dtype != torch.int32:
+            raise TypeError("seqlens must be int32")
+    need = fa_decode_workspace_bytes(B, Hq, Hkv, Nq, Nkv, d, num_splits)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else _nbytes(workspace)
+    st = lib.fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(seqlens), _ptr(o), _ptr(lse), B, Hq, Hkv,
+                       Nq, Nkv, d, float(scale), int(bool(causal)), int(num_splits),
+                       _dtype_code(q), _ptr(workspace), wbytes, _stream(stream))
+    _check(st, "fa_decode")
+
+
 # Convenience wrappers that allocate outputs with torch (memory plumbing only).
+
+def decode(q, k, v, scale: float, seqlens=None, causal: bool = False, num_splits: int = 0,
+           workspace=None, stream=None):
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    fa_decode(q, k, v, o, lse, scale, seqlens, causal, num_splits, workspace, stream)
+    return o, lse
+
+
 
 def forward(q, k, v, scale: float, causal: bool = False, block_mask=None, stream=None):
     o = torch.empty_like(q)

@@ -31,7 +31,8 @@ def test_header_symbols_are_exported(lib):
     names = fa.header_functions()
     assert set(names) == {"fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
                           "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
-                          "fa_fwd_dropout", "fa_bwd_dropout"}
+                          "fa_fwd_dropout", "fa_bwd_dropout", "fa_decode",
+                          "fa_decode_num_splits", "fa_decode_workspace_bytes"}
     out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -133,6 +134,50 @@ def test_dropout_entry_points_check_like_the_plain_ones(lib, kw, code):
     if kw.get("o") is not None and "o" in kw:
         bkw["dq"] = p(0, 64)
     assert bwd_drop(lib, **bkw) == code
+
+
+def test_decode_plan(lib):
+    # 64 sequences x 8 cache heads: four 2048-key chunks (2048 work-groups)
+    assert fa.fa_decode_num_splits(64, 32, 8, 1, 8192, 128) == 4
+    assert fa.fa_decode_workspace_bytes(64, 32, 8, 1, 8192, 128) == 64 * 32 * 4 * 129 * 4
+    # one long sequence: as many chunks as allowed (128 of 1024 keys)
+    assert fa.fa_decode_num_splits(1, 32, 8, 1, 131072, 128) == 128
+    # short caches: one chunk, no workspace
+    assert fa.fa_decode_num_splits(64, 32, 8, 1, 100, 128) == 1
+    assert fa.fa_decode_workspace_bytes(64, 32, 8, 1, 100, 128) == 0
+    # explicit counts are an upper bound; chunks are whole 128-key tiles
+    assert fa.fa_decode_num_splits(2, 4, 4, 1, 1000, 64, num_splits=7) == 4
+    assert fa.fa_decode_num_splits(2, 4, 4, 1, 1000, 64, num_splits=1) == 1
+    assert fa.fa_decode_num_splits(2, 4, 4, 1, 1000, 64, num_splits=100) == 8
+    assert fa.fa_decode_workspace_bytes(2, 4, 4, 3, 1000, 64, num_splits=100) == 2 * 4 * 3 * 8 * 65 * 4
+    # rejected sizes
+    assert fa.fa_decode_num_splits(1, 6, 4, 1, 64, 64) == 0          # Hq not a multiple of Hkv
+    assert fa.fa_decode_num_splits(1, 4, 4, 1, 64, 96) == 0
+    assert fa.fa_decode_num_splits(1, 4, 4, 1, 64, 64, num_splits=1025) == 0
+    assert fa.fa_decode_workspace_bytes(0, 4, 4, 1, 64, 64) == 0
+
+
+def dec(lib, **kw):
+    a = dict(q=p(0), k=p(1), v=p(2), sl=None, o=p(3), lse=p(4), B=2, Hq=8, Hkv=2, Nq=1,
+             Nkv=4096, d=128, scale=0.1, causal=0, ns=0, dtype=BF16, ws=p(9), wsb=1 << 20)
+    a.update(kw)
+    return lib.fa_decode(a["q"], a["k"], a["v"], a["sl"], a["o"], a["lse"], a["B"], a["Hq"],
+                         a["Hkv"], a["Nq"], a["Nkv"], a["d"], a["scale"], a["causal"], a["ns"],
+                         a["dtype"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(v=None), 1), (dict(lse=None), 1),
+    (dict(B=0), 2), (dict(Hkv=3), 2), (dict(Nq=0), 2), (dict(Nkv=0), 2),
+    (dict(Nkv=1 << 24), 2), (dict(d=96), 3), (dict(dtype=5), 4),
+    (dict(q=p(0, 8)), 5), (dict(sl=p(5, 2)), 5), (dict(lse=p(4, 1)), 5),
+    (dict(ws=None), 6), (dict(wsb=100), 6), (dict(ws=p(9, 8)), 6),
+    (dict(scale=float("nan")), 8), (dict(ns=-1), 8), (dict(ns=2000), 8),
+    (dict(o=p(1, 64)), 9), (dict(lse=p(3, 32)), 9), (dict(ws=p(2, 64)), 9),
+    (dict(sl=p(4, 16), ns=1), 9), (dict(o=p(9)), 9),
+])
+def test_decode_validation(lib, kw, code):
+    assert dec(lib, **kw) == code
 
 
 def test_status_codes_match_header():
