@@ -30,20 +30,23 @@
 // new tokens are the last Nq positions, so query row nq sees keys
 // j <= L_b - Nq + nq.  A row that sees no key gets O = 0, LSE = -inf.
 
+#include <algorithm>
+
 #include "fa_common.hpp"
 #include "fa_decode.hpp"
 
 namespace fa {
 
-template <typename T, int D, int WAVES>
+// WAVES waves per work-group (32 keys each per tile), a ring of NBUF [K, V]
+// tile buffers.
+template <typename T, int D, int WAVES, int NBUF>
 struct DecCfg {
   static constexpr int RB = D * (int)sizeof(T);
   static constexpr int KT = 32 * WAVES;                       // keys per tile
   static constexpr int TB = KT * RB;                          // bytes of K (or V) per tile
-  // Ring depth: as many [K, V] tiles as fit in 128 KiB, at most 4.
-  static constexpr int NBUF = 2 * TB * 4 <= 131072 ? 4 : (2 * TB * 3 <= 131072 ? 3 : 2);
   static constexpr int LOADS = 2 * TB / 1024 / WAVES;        // buffer loads per wave per tile
-  static_assert(2 * TB * NBUF <= 131072, "ring must fit in LDS");
+  static_assert(NBUF >= 2 && NBUF <= 4, "ring of 2 to 4 buffers");
+  static_assert(2 * TB * NBUF <= 160 * 1024, "ring must fit in LDS");
   static_assert((NBUF - 2) * LOADS <= 63, "vmcnt immediate is 6 bits");
 };
 
@@ -61,17 +64,17 @@ __device__ __forceinline__ unsigned char* pick4(IntTag<V>, unsigned char* a, uns
   return V == 0 ? a : (V == 1 ? b : (V == 2 ? c : d));
 }
 
-template <typename T, int D, bool CAUSAL, int WAVES>
+template <typename T, int D, bool CAUSAL, int WAVES, int NBUF>
 __global__ void __launch_bounds__(64 * WAVES)
 fa_decode_split_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                        const T* __restrict__ V, const int32_t* __restrict__ seqlens,
                        T* __restrict__ O, float* __restrict__ LSE, float* __restrict__ Opart,
                        float* __restrict__ Lpart, int Hkv, int Nq, int R, int RG, int Nkv,
-                       int S, int chunk, float c /* scale*log2e, > 0 */) {
+                       int S, int chunk, int P, float c /* scale*log2e, > 0 */) {
   using E = Elem<T>;
   using frag = typename E::frag;
-  using Cfg = DecCfg<T, D, WAVES>;
-  constexpr int RB = Cfg::RB, KT = Cfg::KT, TB = Cfg::TB, NBUF = Cfg::NBUF;
+  using Cfg = DecCfg<T, D, WAVES, NBUF>;
+  constexpr int RB = Cfg::RB, KT = Cfg::KT, TB = Cfg::TB;
   constexpr int NT = D / 16, ND = D / 32;
 
   __shared__ __attribute__((aligned(1024))) unsigned char buf0[2 * TB];   // [K, V]
@@ -81,8 +84,19 @@ fa_decode_split_kernel(const T* __restrict__ Q, const T* __restrict__ K,
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
-  const int s = blockIdx.x % S;
-  const int rest = blockIdx.x / S;
+  // Work-group order: blocks of P (batch, cache head, query tile) groups,
+  // about one device-full of work-groups per block; within a block, chunk
+  // index slowest.  So every group's first chunk is dispatched before any
+  // second chunk of its block (the chunks that are empty or short, past the
+  // end of shorter sequences, come last and fill in the tail), while the
+  // work-groups in flight at any time stay within a few blocks of groups.
+  const int PG = (int)(gridDim.x / S);
+  const int blk = blockIdx.x / (P * S);
+  const int pb0 = blk * P;
+  const int Pb = min(P, PG - pb0);
+  const int within = blockIdx.x - pb0 * S;
+  const int s = within / Pb;
+  const int rest = pb0 + (within - s * Pb);
   const int rg = rest % RG;
   const int bkv = rest / RG;                 // b * Hkv + kvh
   const int b = bkv / Hkv;
@@ -124,13 +138,22 @@ fa_decode_split_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   float m_run = neg_inf();   // running max of S*c over this wave's keys (log2 domain)
   float l_run = 0.f;         // this lane's partial row sum
 
+  // bf16: per-lane operand offsets computed once (the compiler then sees
+  // every LDS read as an offset into one named buffer).
+  constexpr bool kBf16 = sizeof(T) == 2;
+  LaneOffsets<T, D> lo;
+  if constexpr (kBf16) lo.init(lane);
+
   auto compute = [&](auto slot, int kv0) {
     const unsigned char* sK = pick4(slot, buf0, buf1, buf2, buf3) + 32 * w * RB;
     const unsigned char* sV = sK + TB;
 
     frag ak[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) ak[t] = row_frag<T, D>(sK, l32, t, g);
+    for (int t = 0; t < NT; ++t) {
+      if constexpr (kBf16) ak[t] = row_frag_at<T>(sK + lo.row[t]);
+      else ak[t] = row_frag<T, D>(sK, l32, t, g);
+    }
     sched_fence();
     f32x16 st = f32x16{};
 #pragma unroll
@@ -167,8 +190,14 @@ fa_decode_split_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     const frag p0 = E::from_c(st, 0), p1 = E::from_c(st, 1);
 #pragma unroll
     for (int bb = 0; bb < ND; ++bb) {
-      const frag a0 = trans_frag<T, D>(sV, bb, 0, lane);
-      const frag a1 = trans_frag<T, D>(sV, bb, 1, lane);
+      frag a0, a1;
+      if constexpr (kBf16) {
+        a0 = trans_frag_at(sV + lo.tr[bb][0], sV + lo.tr[bb][1]);
+        a1 = trans_frag_at(sV + lo.tr[bb][0] + 16 * RB, sV + lo.tr[bb][1] + 16 * RB);
+      } else {
+        a0 = trans_frag<T, D>(sV, bb, 0, lane);
+        a1 = trans_frag<T, D>(sV, bb, 1, lane);
+      }
       oacc[bb] = E::mma(a0, p0, oacc[bb]);
       oacc[bb] = E::mma(a1, p1, oacc[bb]);
     }
@@ -176,7 +205,8 @@ fa_decode_split_kernel(const T* __restrict__ Q, const T* __restrict__ K,
 
   // Ring of NBUF slots, tiles staged NBUF - 1 ahead.  At the top of tile i
   // this wave's loads of tiles i+1 .. i+NBUF-2 may still be in flight; wait
-  // for the rest, then a barrier: all of tile i is in LDS and every wave has
+  // for the rest (vmcnt counts the direct-to-LDS loads until their data is
+  // in LDS), then a barrier: all of tile i is in LDS and every wave has
   // finished tile i-1, whose slot receives tile i+NBUF-1.
   int i = 0;
   auto step = [&](auto slot) -> bool {
@@ -193,7 +223,9 @@ fa_decode_split_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     } else {
       wait_vmcnt<0>();
     }
-    __syncthreads();
+    // A plain barrier: __syncthreads() would also wait for the tiles still
+    // in flight.  The clobber keeps LDS accesses on their side of it.
+    asm volatile("s_barrier" ::: "memory");
     if (i + NBUF - 1 < ntiles) stage(i + NBUF - 1, IntTag<(SL + NBUF - 1) % NBUF>{});
     compute(slot, kb + i * KT);
     ++i;
@@ -296,13 +328,16 @@ fa_decode_combine_kernel(const float* __restrict__ Opart, const float* __restric
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
-  constexpr int WAVES = sizeof(T) == 2 ? 4 : 2;
+  constexpr int WAVES = 2;
+  constexpr int NBUF = 2;
   const int RG = (a.R + 31) / 32;
   const dim3 grid((unsigned)a.pairs * RG * a.S), block(64 * WAVES);
-  hipLaunchKernelGGL((fa_decode_split_kernel<T, D, CAUSAL, WAVES>), grid, block, 0, a.stream,
+  // Groups per ordering block: about 512 work-groups (two per compute unit).
+  const int P = std::max(1, 512 / a.S);
+  hipLaunchKernelGGL((fa_decode_split_kernel<T, D, CAUSAL, WAVES, NBUF>), grid, block, 0, a.stream,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                      static_cast<const T*>(a.v), a.seqlens, static_cast<T*>(a.o), a.lse,
-                     a.opart, a.lpart, a.Hkv, a.Nq, a.R, RG, a.Nkv, a.S, a.chunk,
+                     a.opart, a.lpart, a.Hkv, a.Nq, a.R, RG, a.Nkv, a.S, a.chunk, P,
                      score_coef(a.scale));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.S == 1) return e;
