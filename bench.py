@@ -21,6 +21,12 @@ MFMA 157.3 TFLOP/s for fp32 workloads).
 
 The cpu_baseline leg times the CPU fp64 oracle on a bounded sample of the same
 workload (whole heads, about 10-30 s) on this host's cores.
+
+Decode workloads (--workload decode | decode_mix | decode_spec): a step is one
+fa_decode call over the whole batch (64 sequences, 8K cache, 32 query heads
+over 8 cache heads); value and roofline are algorithmic HBM bytes (visible
+cache rows of K and V once, Q, O, LSE) per second against 8 TB/s, with the HIP
+event pair around the call (its chunk kernel and the merge kernel).
 """
 
 from __future__ import annotations
@@ -69,7 +75,7 @@ def recorded_traffic(workload, kernel):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_hash") != profiles.source_hash() or kernel not in rec:
+    if rec.get("source_hash") != profiles.source_hash(profiles.family(workload)) or kernel not in rec:
         return None
     k = rec[kernel]
     if "read_bytes" not in k or "write_bytes" not in k:
@@ -303,6 +309,15 @@ def cpu_baseline_decode(w, x, budget_s):
     }
 
 
+def decode_traffic(workload, S):
+    """Calibrated HBM bytes of one fa_decode call (its one or two kernels)."""
+    a = recorded_traffic(workload, "fa_decode_split_kernel")
+    if a is None or S == 1:
+        return a
+    b = recorded_traffic(workload, "fa_decode_combine_kernel")
+    return None if b is None else a + b
+
+
 def bench_decode(args):
     """Split-KV decode: one step is one fa_decode call (its chunk kernel and,
     with several chunks, the merge kernel) over the whole batch."""
@@ -353,7 +368,7 @@ def bench_decode(args):
     name = "fa_decode_split_kernel" + (" + fa_decode_combine_kernel" if S > 1 else "")
     roof = {"kernel": name, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-            "traffic": recorded_traffic(w.name, "fa_decode_split_kernel"),
+            "traffic": decode_traffic(w.name, S),
             "algorithmic_bytes_per_launch": by["total"], "avg_launch_ms": avg}
     cpu = None if args.no_cpu else cpu_baseline_decode(w, x, args.cpu_seconds)
     s = sorted(per)

@@ -34,23 +34,39 @@ ROOT = os.path.dirname(HERE)
 PROFILES = os.path.join(ROOT, "profiles")
 
 KERNELS = ("fa_fwd_kernel", "fa_fwd_pp_kernel", "fa_bwd_delta_kernel", "fa_bwd_dkdv_kernel",
-           "fa_bwd_dq_kernel")
+           "fa_bwd_dq_kernel", "fa_decode_split_kernel", "fa_decode_combine_kernel")
+
+# Device sources of each kernel family (host-side files such as fa_api.cpp
+# do not change what a kernel does on the GPU).
+SOURCES = {
+    "train": ("fa_common.hpp", "fa_launch.hpp", "fa_fwd.hip", "fa_bwd.hip"),
+    "decode": ("fa_common.hpp", "fa_decode.hpp", "fa_decode.hip"),
+}
 
 
-def source_hash() -> str:
-    """Hash of the HIP sources the kernels are built from."""
+def family(workload: str) -> str:
+    return "decode" if workload.startswith("decode") else "train"
+
+
+def source_hash(fam: str = "train") -> str:
+    """Hash of the device sources the kernels of family `fam` are built from."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode())
+    for name in SOURCES[fam]:
+        with open(os.path.join(HERE, "csrc", name), "rb") as f:
+            h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+PROBE = "probe:neg"      # bench.py --copy-probe runs one torch.neg over a known size
 
 
 def short_name(kernel_name: str) -> str:
     for k in KERNELS:
         if k in kernel_name:
             return k
+    if "neg_kernel" in kernel_name:
+        return PROBE
     if "copy" in kernel_name.lower() or "elementwise" in kernel_name:
         return "copy:" + kernel_name[:60]
     return kernel_name[:60]
@@ -89,8 +105,8 @@ def traffic(fetch_dir: str, write_dir: str, copy_bytes: int) -> dict:
     out = {}
     for counter, d, key in (("FETCH_SIZE", fetch_dir, "read"), ("WRITE_SIZE", write_dir, "write")):
         per = _counter_per_kernel(d, counter)
-        copies = [v for k, vs in per.items() if k.startswith("copy:") for v in vs]
-        probe = max(copies) if copies else None        # the big copy is the probe
+        copies = per.get(PROBE, [])
+        probe = max(copies) if copies else None
         factor = copy_bytes / (probe * 1024.0) if probe else None
         out[f"{key}_calibration"] = {"probe_bytes": copy_bytes,
                                      "counter_kib": probe, "factor": factor}
@@ -193,7 +209,7 @@ def main(argv):
         fetch_dir, write_dir, workload, out_path, cmd_f, cmd_w = argv[1:7]
         copy_bytes = int(os.environ.get("FA_COPY_PROBE_BYTES", 512 << 20))
         t = traffic(fetch_dir, write_dir, copy_bytes)
-        t.update({"workload": workload, "source_hash": source_hash(),
+        t.update({"workload": workload, "source_hash": source_hash(family(workload)),
                   "commands": {"FETCH_SIZE": cmd_f, "WRITE_SIZE": cmd_w}})
         json.dump(t, open(out_path, "w"), indent=1)
         print(json.dumps(t, indent=1))
