@@ -33,3 +33,4 @@ from .online import (  # noqa: F401
     tiled_forward_deferred,
 )
 from . import decode  # noqa: F401
+from . import gqa  # noqa: F401
