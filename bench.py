@@ -98,7 +98,9 @@ def cpu_baseline(w, x, budget_s):
     t0 = time.perf_counter()
     for b, h in heads:
         sl = (slice(b, b + 1), slice(h, h + 1))
-        oracle.forward_backward(x["q"][sl], x["k"][sl], x["v"][sl], x["do"][sl], w.scale,
+        c = h // (w.H // w.kv_heads)                       # its key/value head
+        kv = (slice(b, b + 1), slice(c, c + 1))
+        oracle.forward_backward(x["q"][sl], x["k"][kv], x["v"][kv], x["do"][sl], w.scale,
                                 w.causal, x["mask"])
         done += 1
         if time.perf_counter() - t0 >= budget_s:
@@ -154,9 +156,21 @@ def main():
         del src, dst
 
     drop = args.dropout
-    phases = ["fwd", "bwd"] if drop > 0 else ["fwd", "pre", "dkdv", "dq"]
+    grouped = w.Hkv is not None and w.Hkv != w.H
+    if grouped and drop > 0:
+        print("--dropout is not offered for grouped key/value heads", file=sys.stderr)
+        sys.exit(2)
+    phases = ["fwd", "bwd"] if (drop > 0 or grouped) else ["fwd", "pre", "dkdv", "dq"]
 
     def step(ev=None):
+        if grouped:
+            # fa_fwd_gqa, then fa_bwd_gqa (its three kernels in one entry point)
+            if ev: ev[0].record()
+            fa.fa_fwd_gqa(q, k, v, o, lse, sc, cz, mask)
+            if ev: ev[1].record()
+            fa.fa_bwd_gqa(q, k, v, o, do, lse, dq, dk, dv, sc, cz, mask, ws)
+            if ev: ev[2].record()
+            return
         if drop > 0:
             # the backward's three kernels run inside one entry point here
             if ev: ev[0].record()
@@ -207,7 +221,8 @@ def main():
     fwd_name = ("fa_fwd_pp_kernel" if w.dtype == "bf16" and w.d == 128 and w.mask_density is None
                 and drop == 0 else "fa_fwd_kernel")
     names = {"fwd": fwd_name, "pre": "fa_bwd_delta_kernel", "dkdv": "fa_bwd_dkdv_kernel",
-             "dq": "fa_bwd_dq_kernel", "bwd": "fa_bwd_dropout (three kernels)"}
+             "dq": "fa_bwd_dq_kernel",
+             "bwd": ("fa_bwd_gqa" if grouped else "fa_bwd_dropout") + " (three kernels)"}
     dom = max(phases, key=lambda p: avg[p])
     if dom == "pre":
         ach = hb["pre_kernel"] / (avg[dom] * 1e-3) / 1e9
@@ -231,7 +246,7 @@ def main():
         kernels[names[p]] = entry
 
     fwd_ms = avg["fwd"]
-    bwd_ms = avg["bwd"] if drop > 0 else avg["pre"] + avg["dkdv"] + avg["dq"]
+    bwd_ms = avg["bwd"] if "bwd" in avg else avg["pre"] + avg["dkdv"] + avg["dq"]
     s = sorted(steps_ms)
     n = len(s)
     mean = statistics.mean(s)
@@ -257,7 +272,8 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded iid normal Q, K, V, dO)",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.kv_heads, "N": w.N,
+                   "d": w.d,
                    "causal": w.causal, "block_sparse": x["mask"] is not None,
                    "dropout": drop,
                    "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)"},

@@ -183,6 +183,32 @@ fa_status fa_bwd_dropout(const void* Q, const void* K, const void* V, const void
                          size_t workspace_bytes, void* stream);
 
 /*
+ * fa_fwd_gqa / fa_bwd_gqa -- fa_fwd and fa_bwd with grouped key/value heads
+ * (GQA; MQA when Hkv = 1): query heads h = kvh*G .. kvh*G+G-1, G = Hq / Hkv,
+ * all attend with key/value head kvh (the week-13 page,
+ * snula.amonoc.com/course/ru/week-13.html, names GQA: one key/value head per
+ * group of query heads).  The forward and dQ are those of fa_fwd / fa_bwd per
+ * query head; a shared head's dK and dV are the sums over its G query heads,
+ * accumulated on chip by one work-group per 128 keys that walks the tiles of
+ * all G heads (no atomics; deterministic).
+ *
+ *   Q, O, dO, dQ : [B, Hq, N, d] dtype;  LSE: [B, Hq, N] fp32
+ *   K, V, dK, dV : [B, Hkv, N, d] dtype (dK, dV overwritten)
+ *   workspace    : at least fa_bwd_workspace_bytes(B, Hq, N, d) bytes
+ * Hq must be a multiple of Hkv (FA_ERR_SHAPE otherwise); other arguments and
+ * checks as for fa_fwd / fa_bwd (with H = Hq).  Hkv = Hq gives exactly
+ * fa_fwd / fa_bwd.
+ */
+fa_status fa_fwd_gqa(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                     int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                     const unsigned char* block_mask, fa_dtype dtype, void* stream);
+fa_status fa_bwd_gqa(const void* Q, const void* K, const void* V, const void* O,
+                     const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                     int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                     const unsigned char* block_mask, fa_dtype dtype, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
  * fa_decode -- attention of a few new query rows against a key/value cache,
  * with grouped key/value heads (inference decode; the week-13 page's note on
  * decode attention and GQA, snula.amonoc.com/course/ru/week-13.html).

@@ -111,22 +111,29 @@ fa_status dropout_params(float p, unsigned long long seed, fa::Dropout* out) {
 }
 
 fa_status fwd_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
-                   int H, int N, int d, float scale, int causal, const unsigned char* block_mask,
-                   fa_dtype dtype, const fa::Dropout& drop, void* stream);
+                   int H, int Hkv, int N, int d, float scale, int causal,
+                   const unsigned char* block_mask, fa_dtype dtype, const fa::Dropout& drop,
+                   void* stream);
 
 fa_status bwd_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO,
-                   const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int N, int d,
-                   float scale, int causal, const unsigned char* block_mask, fa_dtype dtype,
-                   void* workspace, size_t workspace_bytes, const fa::Dropout& drop,
-                   void* stream);
+                   const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int Hkv, int N,
+                   int d, float scale, int causal, const unsigned char* block_mask,
+                   fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                   const fa::Dropout& drop, void* stream);
+
+// Key/value head count: >= 1 and dividing the query head count.
+fa_status check_kv_heads(int H, int Hkv) {
+  if (Hkv < 1 || H < 1 || H % Hkv) return FA_ERR_SHAPE;
+  return FA_OK;
+}
 
 }  // namespace
 
 FA_EXPORT fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
                            int B, int H, int N, int d, float scale, int causal,
                            const unsigned char* block_mask, fa_dtype dtype, void* stream) {
-  return fwd_impl(Q, K, V, O, LSE, B, H, N, d, scale, causal, block_mask, dtype, fa::Dropout{},
-                  stream);
+  return fwd_impl(Q, K, V, O, LSE, B, H, H, N, d, scale, causal, block_mask, dtype,
+                  fa::Dropout{}, stream);
 }
 
 FA_EXPORT fa_status fa_fwd_dropout(const void* Q, const void* K, const void* V, void* O,
@@ -137,19 +144,23 @@ FA_EXPORT fa_status fa_fwd_dropout(const void* Q, const void* K, const void* V, 
   FA_TRY(check_buffers({{Q, 0, 0}, {K, 0, 0}, {V, 0, 0}}, {{O, 0, 0}, {LSE, 0, 0}}));
   FA_TRY(check_shape(Shape{B, H, N, d, dtype}, scale));
   FA_TRY(dropout_params(dropout_p, seed, &drop));
-  return fwd_impl(Q, K, V, O, LSE, B, H, N, d, scale, causal, block_mask, dtype, drop, stream);
+  return fwd_impl(Q, K, V, O, LSE, B, H, H, N, d, scale, causal, block_mask, dtype, drop,
+                  stream);
 }
 
 namespace {
 
 fa_status fwd_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
-                   int H, int N, int d, float scale, int causal, const unsigned char* block_mask,
-                   fa_dtype dtype, const fa::Dropout& drop, void* stream) {
+                   int H, int Hkv, int N, int d, float scale, int causal,
+                   const unsigned char* block_mask, fa_dtype dtype, const fa::Dropout& drop,
+                   void* stream) {
   FA_TRY(check_buffers({{Q, 0, 0}, {K, 0, 0}, {V, 0, 0}}, {{O, 0, 0}, {LSE, 0, 0}}));
   const Shape s{B, H, N, d, dtype};
   FA_TRY(check_shape(s, scale));
+  FA_TRY(check_kv_heads(H, Hkv));
   const uintptr_t tb = s.tensor_bytes(), lb = s.row_bytes();
-  const Buf q{Q, tb, 16}, k{K, tb, 16}, v{V, tb, 16}, o{O, tb, 16}, l{LSE, lb, 4};
+  const uintptr_t kvb = tb / H * Hkv;
+  const Buf q{Q, tb, 16}, k{K, kvb, 16}, v{V, kvb, 16}, o{O, tb, 16}, l{LSE, lb, 4};
   const Buf m{block_mask, block_mask ? s.mask_bytes() : 0, 1};
   FA_TRY(check_layout({q, k, v, m}, {o, l}, nullptr, false, 0));
 
@@ -157,6 +168,7 @@ fa_status fwd_impl(const void* Q, const void* K, const void* V, void* O, float* 
   a.q = Q; a.k = K; a.v = V; a.o = O; a.lse = LSE;
   a.mask = block_mask;
   a.BH = B * H; a.N = N; a.d = d; a.T = (N + 127) / 128;
+  a.G = H / Hkv;
   a.scale = scale;
   a.causal = causal != 0;
   a.bf16 = dtype == FA_BF16;
@@ -231,8 +243,8 @@ FA_EXPORT fa_status fa_bwd(const void* Q, const void* K, const void* V, const vo
                            int B, int H, int N, int d, float scale, int causal,
                            const unsigned char* block_mask, fa_dtype dtype, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  return bwd_impl(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, N, d, scale, causal, block_mask, dtype,
-                  workspace, workspace_bytes, fa::Dropout{}, stream);
+  return bwd_impl(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, H, N, d, scale, causal, block_mask,
+                  dtype, workspace, workspace_bytes, fa::Dropout{}, stream);
 }
 
 FA_EXPORT fa_status fa_bwd_dropout(const void* Q, const void* K, const void* V, const void* O,
@@ -246,29 +258,48 @@ FA_EXPORT fa_status fa_bwd_dropout(const void* Q, const void* K, const void* V, 
                        {{dQ, 0, 0}, {dK, 0, 0}, {dV, 0, 0}}));
   FA_TRY(check_shape(Shape{B, H, N, d, dtype}, scale));
   FA_TRY(dropout_params(dropout_p, seed, &drop));
-  return bwd_impl(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, N, d, scale, causal, block_mask, dtype,
-                  workspace, workspace_bytes, drop, stream);
+  return bwd_impl(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, H, N, d, scale, causal, block_mask,
+                  dtype, workspace, workspace_bytes, drop, stream);
+}
+
+FA_EXPORT fa_status fa_fwd_gqa(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                               int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                               const unsigned char* block_mask, fa_dtype dtype, void* stream) {
+  return fwd_impl(Q, K, V, O, LSE, B, Hq, Hkv, N, d, scale, causal, block_mask, dtype,
+                  fa::Dropout{}, stream);
+}
+
+FA_EXPORT fa_status fa_bwd_gqa(const void* Q, const void* K, const void* V, const void* O,
+                               const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                               int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                               const unsigned char* block_mask, fa_dtype dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return bwd_impl(Q, K, V, O, dO, LSE, dQ, dK, dV, B, Hq, Hkv, N, d, scale, causal, block_mask,
+                  dtype, workspace, workspace_bytes, fa::Dropout{}, stream);
 }
 
 namespace {
 
 fa_status bwd_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO,
-                   const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int N, int d,
-                   float scale, int causal, const unsigned char* block_mask, fa_dtype dtype,
-                   void* workspace, size_t workspace_bytes, const fa::Dropout& drop,
-                   void* stream) {
+                   const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int Hkv, int N,
+                   int d, float scale, int causal, const unsigned char* block_mask,
+                   fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                   const fa::Dropout& drop, void* stream) {
   FA_TRY(check_buffers({{Q, 0, 0}, {K, 0, 0}, {V, 0, 0}, {O, 0, 0}, {dO, 0, 0}, {LSE, 0, 0}},
                        {{dQ, 0, 0}, {dK, 0, 0}, {dV, 0, 0}}));
   const Shape s{B, H, N, d, dtype};
   FA_TRY(check_shape(s, scale));
+  FA_TRY(check_kv_heads(H, Hkv));
   const uintptr_t tb = s.tensor_bytes(), lb = s.row_bytes();
+  const uintptr_t kvb = tb / H * Hkv;
   const Buf ws{workspace, workspace_bytes, 16};
   const Buf m{block_mask, block_mask ? s.mask_bytes() : 0, 1};
   FA_TRY(check_layout(
-      {{Q, tb, 16}, {K, tb, 16}, {V, tb, 16}, {O, tb, 16}, {dO, tb, 16}, {LSE, lb, 4}, m},
-      {{dQ, tb, 16}, {dK, tb, 16}, {dV, tb, 16}}, &ws, true, lb));
+      {{Q, tb, 16}, {K, kvb, 16}, {V, kvb, 16}, {O, tb, 16}, {dO, tb, 16}, {LSE, lb, 4}, m},
+      {{dQ, tb, 16}, {dK, kvb, 16}, {dV, kvb, 16}}, &ws, true, lb));
 
   fa::BwdArgs a = bwd_args(s, scale, causal, block_mask, stream);
+  a.G = H / Hkv;
   a.q = Q; a.k = K; a.v = V; a.o = O; a.dout = dO; a.lse = LSE;
   a.dq = dQ; a.dk = dK; a.dv = dV;
   a.delta = static_cast<float*>(workspace);

@@ -78,8 +78,8 @@ __attribute__((amdgpu_waves_per_eu(1, 1)))
 fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                    const T* __restrict__ dO, const float* __restrict__ LSE,
                    const float* __restrict__ delta, T* __restrict__ dK, T* __restrict__ dV,
-                   const uint8_t* __restrict__ mask, int BH, int N, int T_tiles, float c,
-                   float scale, DropParams drp) {
+                   const uint8_t* __restrict__ mask, int BH, int kv_group, int N, int T_tiles,
+                   float c, float scale, DropParams drp) {
   using E = Elem<T>;
   using frag = typename E::frag;
   using Cfg = DkdvCfg<T>;
@@ -100,11 +100,11 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
   const int nkb = (N + BK - 1) / BK;
+  // BH counts key/value heads here; query heads bh*kv_group .. +kv_group-1
+  // share head bh, and their contributions to dK, dV are summed on chip.
   const BlockCoord bc = map_block(blockIdx.x, nkb, BH, CAUSAL, false);
   const int bh = bc.bh, kb = bc.blk, k0 = kb * BK;
-  const size_t head = (size_t)bh * N * D;
-  const T* Qh = Q + head;
-  const T* dOh = dO + head;
+  const size_t head = (size_t)bh * N * D;   // K, V, dK, dV of this key/value head
   const int kw = k0 + 32 * w;            // this wave's first key
   const int krow = kw + l32;             // this lane's key
 
@@ -133,12 +133,29 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
     return i;
   };
 
-  const rsrc_t rl = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
-  const rsrc_t rd = make_rsrc(delta + (size_t)bh * N, (uint32_t)N * 4);
+  // The walk covers (query head of the group, staged tile) pairs u =
+  // gq * ntiles + i, kept tiles only.
+  const int NU = kv_group * ntiles;
+  auto next_u = [&](int u) {
+    while (u < NU) {
+      const int gq = u / ntiles;
+      const int k = next_kept(max(u - gq * ntiles, first));
+      if (k < ntiles) return gq * ntiles + k;
+      u = (gq + 1) * ntiles;
+    }
+    return NU;
+  };
+
   float lpre = 0.f, dpre = 0.f;     // row statistics of the tile in flight (threads < SQ)
   int lrow_pre = 0;
-  auto stage = [&](int i, auto buf) {
-    const int q0 = i * SQ;
+  auto stage = [&](int u, auto buf) {
+    const int gq = u / ntiles;
+    const int q0 = (u - gq * ntiles) * SQ;
+    const size_t hq = (size_t)bh * kv_group + gq;      // query head
+    const T* Qh = Q + hq * N * D;
+    const T* dOh = dO + hq * N * D;
+    const rsrc_t rl = make_rsrc(LSE + hq * N, (uint32_t)N * 4);
+    const rsrc_t rd = make_rsrc(delta + hq * N, (uint32_t)N * 4);
     const uint32_t left = (uint32_t)(N - q0) * RB;
     unsigned char* base = pick(buf, lds0, lds1);
     stage_tile<T, D, SQ>(make_rsrc(Qh + (size_t)q0 * D, left), base, w, lane);
@@ -155,6 +172,7 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   for (int b = 0; b < ND; ++b) { dkacc[b] = f32x16{}; dvacc[b] = f32x16{}; }
   LaneOffsets<T, D> lo;
   lo.init(lane);
+  int bhq = bh * kv_group;   // query head of the tile being computed
 
   // One tile iteration.  MASKED_TILE (the tile crosses this wave's causal
   // diagonal) is compile-time, so unmasked tiles carry no mask arithmetic.
@@ -214,7 +232,7 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
               // dV takes the dropped probabilities (its 1/(1-p) is applied at
               // the end); dS = P (dP M - D) with M = Z / (1-p).
               const Philox4 z = philox4x32_10((uint32_t)krow >> 2, (uint32_t)(q0 + qi + x),
-                                              (uint32_t)bh, 0u, drp.key0, drp.key1);
+                                              (uint32_t)bhq, 0u, drp.key0, drp.key1);
               const uint32_t word = (krow & 2) ? ((krow & 1) ? z.w[3] : z.w[2])
                                                : ((krow & 1) ? z.w[1] : z.w[0]);
               const bool keep = word >= drp.thresh;
@@ -329,8 +347,11 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   };
   // Wait for tile i (buffer BUF), publish its row statistics, prefetch the
   // next kept tile into the other buffer, then run the tile.
-  auto step = [&](auto buf_sel, int i, int in) {
+  auto step = [&](auto buf_sel, int u, int un) {
     const int BUF = buf_sel;
+    const int gq = u / ntiles;
+    const int i = u - gq * ntiles;
+    bhq = bh * kv_group + gq;
     wait_global_loads();
     if (tid < SQ) {
       // Rows past N, and rows that keep no key (LSE = -inf), get P = 0.
@@ -338,7 +359,7 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
       sD[BUF][tid] = dpre;
     }
     __syncthreads();
-    if (in < ntiles) stage(in, other(buf_sel));
+    if (un < NU) stage(un, other(buf_sel));
 #pragma unroll 1
     for (int sub = 0; sub < SQ / BQ; ++sub) {
       const int q0 = i * SQ + sub * BQ;
@@ -352,27 +373,27 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
     }
   };
 
-  int i = next_kept(first);
-  if (i < ntiles) stage(i, IntTag<0>{});
+  int u = next_u(0);
+  if (u < NU) stage(u, IntTag<0>{});
   if constexpr (sizeof(T) == 2) {
     // Two iterations per trip with the buffer index a compile-time constant,
     // so the LDS offsets are immediates.
-    while (i < ntiles) {
-      int in = next_kept(i + 1);
-      step(IntTag<0>{}, i, in);
-      i = in;
-      if (i >= ntiles) break;
-      in = next_kept(i + 1);
-      step(IntTag<1>{}, i, in);
-      i = in;
+    while (u < NU) {
+      int un = next_u(u + 1);
+      step(IntTag<0>{}, u, un);
+      u = un;
+      if (u >= NU) break;
+      un = next_u(u + 1);
+      step(IntTag<1>{}, u, un);
+      u = un;
     }
   } else {
     int buf = 0;
-    while (i < ntiles) {
-      const int in = next_kept(i + 1);
-      step(buf, i, in);
+    while (u < NU) {
+      const int un = next_u(u + 1);
+      step(buf, u, un);
       buf ^= 1;
-      i = in;
+      u = un;
     }
   }
 
@@ -414,8 +435,8 @@ __attribute__((amdgpu_waves_per_eu(Occupancy<T, D>::dq, Occupancy<T, D>::dq)))
 fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                  const T* __restrict__ dO, const float* __restrict__ LSE,
                  const float* __restrict__ delta, T* __restrict__ dQ,
-                 const uint8_t* __restrict__ mask, int BH, int N, int T_tiles, float c,
-                 float scale, DropParams drp) {
+                 const uint8_t* __restrict__ mask, int BH, int kv_group, int N, int T_tiles,
+                 float c, float scale, DropParams drp) {
   using E = Elem<T>;
   using frag = typename E::frag;
   using Cfg = DqCfg<T>;
@@ -434,8 +455,9 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   const BlockCoord bc = map_block(blockIdx.x, nqb, BH, CAUSAL, true);
   const int bh = bc.bh, q0 = bc.blk * BR;
   const size_t head = (size_t)bh * N * D;
-  const T* Kh = K + head;
-  const T* Vh = V + head;
+  const size_t kvhead = (size_t)(bh / kv_group) * N * D;    // shared key/value head
+  const T* Kh = K + kvhead;
+  const T* Vh = V + kvhead;
   const int qrow = q0 + 32 * w + l32;
 
   const rsrc_t rq = make_rsrc(Q + head, (uint32_t)N * RB);
@@ -635,11 +657,12 @@ template <typename T, int D, bool CAUSAL, bool MASKED>
 static hipError_t launch_dkdv_t(const BwdArgs& a) {
   const int nkb = (a.N + DkdvCfg<T>::BK - 1) / DkdvCfg<T>::BK;
   auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3(nkb * a.BH), dim3(kThreads), 0, a.stream,
+    const int bh_kv = a.BH / a.G;     // one work-group row per key/value head
+    hipLaunchKernelGGL(kernel, dim3(nkb * bh_kv), dim3(kThreads), 0, a.stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
-                       static_cast<T*>(a.dk), static_cast<T*>(a.dv), a.mask, a.BH, a.N, a.T,
-                       score_coef(a.scale), a.scale, drop_params(a));
+                       static_cast<T*>(a.dk), static_cast<T*>(a.dv), a.mask, bh_kv, a.G, a.N,
+                       a.T, score_coef(a.scale), a.scale, drop_params(a));
   };
   if (a.drop.on) go(fa_bwd_dkdv_kernel<T, D, CAUSAL, MASKED, true>);
   else go(fa_bwd_dkdv_kernel<T, D, CAUSAL, MASKED, false>);
@@ -653,7 +676,7 @@ static hipError_t launch_dq_t(const BwdArgs& a) {
     hipLaunchKernelGGL(kernel, dim3(nqb * a.BH), dim3(kThreads), 0, a.stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
-                       static_cast<T*>(a.dq), a.mask, a.BH, a.N, a.T, score_coef(a.scale),
+                       static_cast<T*>(a.dq), a.mask, a.BH, a.G, a.N, a.T, score_coef(a.scale),
                        a.scale, drop_params(a));
   };
   if (a.drop.on) go(fa_bwd_dq_kernel<T, D, CAUSAL, MASKED, true>);

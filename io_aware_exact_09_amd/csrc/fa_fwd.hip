@@ -42,7 +42,8 @@ __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(Occupancy<T, D>::fwd, Occupancy<T, D>::fwd)))
 fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
               T* __restrict__ O, float* __restrict__ LSE, const uint8_t* __restrict__ mask,
-              int BH, int N, int T_tiles, float c /* scale*log2e, > 0 */, DropParams dp) {
+              int BH, int kv_group, int N, int T_tiles, float c /* scale*log2e, > 0 */,
+              DropParams dp) {
   using E = Elem<T>;
   using frag = typename E::frag;
   using Cfg = FwdCfg<T>;
@@ -63,8 +64,9 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   const BlockCoord bc = map_block(blockIdx.x, nqb, BH, CAUSAL, true);
   const int bh = bc.bh, q0 = bc.blk * BR;
   const size_t head = (size_t)bh * N * D;
-  const T* Kh = K + head;
-  const T* Vh = V + head;
+  const size_t kvhead = (size_t)(bh / kv_group) * N * D;    // shared key/value head
+  const T* Kh = K + kvhead;
+  const T* Vh = V + kvhead;
   const int qrow = q0 + 32 * w + l32;
 
   // Query fragments (B operand, natural order): Q[qrow][16t + 8g .. +7];
@@ -271,12 +273,12 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
     hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, MASKED, true>), grid, block, 0, a.stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), static_cast<T*>(a.o), a.lse, a.mask, a.BH,
-                       a.N, a.T, score_coef(a.scale), dp);
+                       a.G, a.N, a.T, score_coef(a.scale), dp);
   else
     hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, MASKED, false>), grid, block, 0, a.stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), static_cast<T*>(a.o), a.lse, a.mask, a.BH,
-                       a.N, a.T, score_coef(a.scale), dp);
+                       a.G, a.N, a.T, score_coef(a.scale), dp);
   return hipGetLastError();
 }
 
@@ -309,7 +311,7 @@ template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(2 * kThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd_pp_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-                 T* __restrict__ O, float* __restrict__ LSE, int BH, int N,
+                 T* __restrict__ O, float* __restrict__ LSE, int BH, int kv_group, int N,
                  float c /* scale*log2e, > 0 */) {
   static_assert(sizeof(T) == 2, "bf16 only");
   using E = Elem<T>;
@@ -330,8 +332,9 @@ fa_fwd_pp_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   const BlockCoord bc = map_block(blockIdx.x, nqb, BH, CAUSAL, true);
   const int bh = bc.bh, q0 = bc.blk * BR;
   const size_t head = (size_t)bh * N * D;
-  const T* Kh = K + head;
-  const T* Vh = V + head;
+  const size_t kvhead = (size_t)(bh / kv_group) * N * D;    // shared key/value head
+  const T* Kh = K + kvhead;
+  const T* Vh = V + kvhead;
   const int row0 = q0 + 128 * G + 32 * wg;     // this wave's first row
   const int qrow = row0 + l32;
 
@@ -508,7 +511,7 @@ static hipError_t launch_fwd_pp(const FwdArgs& a) {
   const int nqb = (a.N + 255) / 256;
   hipLaunchKernelGGL((fa_fwd_pp_kernel<T, D, CAUSAL>), dim3(nqb * a.BH), dim3(2 * kThreads), 0,
                      a.stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                     static_cast<const T*>(a.v), static_cast<T*>(a.o), a.lse, a.BH, a.N,
+                     static_cast<const T*>(a.v), static_cast<T*>(a.o), a.lse, a.BH, a.G, a.N,
                      score_coef(a.scale));
   return hipGetLastError();
 }

@@ -22,7 +22,8 @@ struct FwdArgs {
   const void* q; const void* k; const void* v;
   void* o; float* lse;
   const uint8_t* mask;     // nullptr = dense
-  int BH, N, d, T;         // T = ceil(N / 128) (mask side)
+  int BH, N, d, T;         // BH = B * (query heads); T = ceil(N / 128) (mask side)
+  int G = 1;               // query heads per key/value head (K, V have BH / G heads)
   float scale;
   bool causal, bf16;
   Dropout drop;
@@ -35,7 +36,8 @@ struct BwdArgs {
   void* dq; void* dk; void* dv;
   float* delta;            // workspace: D_i = rowsum(dO * O), [BH * N] fp32
   const uint8_t* mask;
-  int BH, N, d, T;
+  int BH, N, d, T;         // BH = B * (query heads)
+  int G = 1;               // query heads per key/value head (K, V, dK, dV have BH / G heads)
   float scale;
   bool causal, bf16;
   Dropout drop;

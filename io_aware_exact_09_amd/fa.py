@@ -76,6 +76,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp,
                                        f, u64, i, vp, sz, vp]
         lib.fa_bwd_dropout.restype = i
+        lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp]
+        lib.fa_fwd_gqa.restype = i
+        lib.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp,
+                                   i, vp, sz, vp]
+        lib.fa_bwd_gqa.restype = i
         lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, sz,
                                   vp]
         lib.fa_decode.restype = i
@@ -255,6 +260,36 @@ def fa_bwd_dq(q, k, v, do, lse, dq, scale, causal=False, block_mask=None, worksp
                        float(scale), int(bool(causal)), _ptr(block_mask), _dtype_code(q),
                        _ptr(workspace), _nbytes(workspace), _stream(stream))
     _check(st, "fa_bwd_dq")
+
+
+def fa_fwd_gqa(q, k, v, o, lse, scale: float, causal: bool = False, block_mask=None,
+               stream=None) -> None:
+    """Forward with grouped key/value heads: q, o [B,Hq,N,d]; k, v [B,Hkv,N,d]."""
+    lib = load_library()
+    _check_tensors(q, dict(q=q, k=k, v=v, o=o, lse=lse))
+    _mask_ok(q, block_mask)
+    B, Hq, N, d = q.shape
+    st = lib.fa_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, k.shape[1], N, d,
+                        float(scale), int(bool(causal)), _ptr(block_mask), _dtype_code(q),
+                        _stream(stream))
+    _check(st, "fa_fwd_gqa")
+
+
+def fa_bwd_gqa(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = False,
+               block_mask=None, workspace=None, stream=None) -> None:
+    """Backward with grouped key/value heads (dk, dv: [B,Hkv,N,d])."""
+    lib = load_library()
+    _check_tensors(q, dict(q=q, k=k, v=v, o=o, do=do, lse=lse, dq=dq, dk=dk, dv=dv))
+    _mask_ok(q, block_mask)
+    B, Hq, N, d = q.shape
+    if workspace is None:
+        workspace = torch.empty(max(fa_bwd_workspace_bytes(B, Hq, N, d), 1), dtype=torch.uint8,
+                                device=q.device)
+    st = lib.fa_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                        _ptr(dk), _ptr(dv), B, Hq, k.shape[1], N, d, float(scale),
+                        int(bool(causal)), _ptr(block_mask), _dtype_code(q), _ptr(workspace),
+                        _nbytes(workspace), _stream(stream))
+    _check(st, "fa_bwd_gqa")
 
 
 def fa_decode_num_splits(B, Hq, Hkv, Nq, Nkv, d, num_splits=0) -> int:

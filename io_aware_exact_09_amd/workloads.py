@@ -15,10 +15,13 @@ The five workloads stand in for the shapes the FlashAttention reading guide
   sparse    B=4  H=8  N=8192  d=64   bf16  128-tile block mask, Bernoulli(0.25)
                                            keep pattern plus the diagonal
   verylong  B=1  H=8  N=16384 d=128  bf16  causal         sigma = 0.5
+  long_gqa  as long (without the x20 rows), 4 key/value heads shared by
+            the 16 query heads
 
 Recipe (the same for every workload): ``rng = numpy.random.default_rng(seed)``
 (PCG64); draw Q, K, V, dO in that order, each
-``rng.standard_normal((B, H, N, d), dtype=float32) * sigma``; then, for
+``rng.standard_normal((B, H, N, d), dtype=float32) * sigma`` (K and V with the
+key/value head count when it differs); then, for
 ``long``, choose floor(0.01 * B*H*N) rows of the flattened [B*H*N] K row index
 without replacement and multiply those rows by 20; then, for ``sparse``, draw
 the [T, T] keep pattern (T = ceil(N/128)) as ``rng.random((T, T)) < 0.25`` and
@@ -52,6 +55,11 @@ class Workload:
     k_row_gain: float = 1.0
     mask_density: Optional[float] = None   # Bernoulli keep probability
     seed: int = 0
+    Hkv: Optional[int] = None  # key/value heads when grouped (None: H, one per query head)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H if self.Hkv is None else self.Hkv
 
     @property
     def scale(self) -> float:
@@ -74,6 +82,10 @@ WORKLOADS = {
                        mask_density=0.25, seed=1004),
     "verylong": Workload("verylong", 1, 8, 16384, 128, "bf16", True,
                          sigma=0.5, seed=1005),
+    # long-context training with grouped key/value heads (4 query heads per
+    # key/value head, the grouping of the week-13 page's Llama-3-8B example),
+    # iid N(0, 1) inputs
+    "long_gqa": Workload("long_gqa", 2, 16, 4096, 128, "bf16", True, seed=1006, Hkv=4),
 }
 
 
@@ -169,12 +181,13 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
     """
     rng = np.random.default_rng(w.seed if seed is None else seed)
     shape = (w.B, w.H, w.N, w.d)
+    kv_shape = (w.B, w.kv_heads, w.N, w.d)
     q = rng.standard_normal(shape, dtype=np.float32) * np.float32(w.sigma)
-    k = rng.standard_normal(shape, dtype=np.float32) * np.float32(w.sigma)
-    v = rng.standard_normal(shape, dtype=np.float32) * np.float32(w.sigma)
+    k = rng.standard_normal(kv_shape, dtype=np.float32) * np.float32(w.sigma)
+    v = rng.standard_normal(kv_shape, dtype=np.float32) * np.float32(w.sigma)
     do = rng.standard_normal(shape, dtype=np.float32) * np.float32(w.sigma)
     if w.k_row_frac > 0.0:
-        rows_total = w.B * w.H * w.N
+        rows_total = w.B * w.kv_heads * w.N
         count = int(math.floor(w.k_row_frac * rows_total))
         idx = rng.choice(rows_total, size=count, replace=False)
         flat = k.reshape(rows_total, w.d)

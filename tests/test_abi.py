@@ -31,7 +31,8 @@ def test_header_symbols_are_exported(lib):
     names = fa.header_functions()
     assert set(names) == {"fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
                           "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
-                          "fa_fwd_dropout", "fa_bwd_dropout", "fa_decode",
+                          "fa_fwd_dropout", "fa_bwd_dropout", "fa_decode", "fa_fwd_gqa",
+                          "fa_bwd_gqa",
                           "fa_decode_num_splits", "fa_decode_workspace_bytes"}
     out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -134,6 +135,27 @@ def test_dropout_entry_points_check_like_the_plain_ones(lib, kw, code):
     if kw.get("o") is not None and "o" in kw:
         bkw["dq"] = p(0, 64)
     assert bwd_drop(lib, **bkw) == code
+
+
+def test_gqa_validation(lib):
+    # fwd: (Q, K, V, O, LSE, B, Hq, Hkv, N, d, scale, causal, mask, dtype, stream)
+    f = [p(0), p(1), p(2), p(3), p(4), 2, 8, 2, 128, 64, 0.125, 1, None, BF16, None]
+    for idx, val, code in ((6, 7, 2), (7, 3, 2), (7, 0, 2), (7, 16, 2), (0, None, 1),
+                           (9, 80, 3), (13, 9, 4), (10, -1.0, 8), (3, p(1, 64), 9)):
+        bad = list(f); bad[idx] = val
+        assert lib.fa_fwd_gqa(*bad) == code, (idx, val)
+    # K spans B * Hkv heads: an output starting inside its last head overlaps it
+    kv_bytes = 2 * 2 * 128 * 64 * 2
+    bad = list(f); bad[3] = p(1, kv_bytes - 16)
+    assert lib.fa_fwd_gqa(*bad) == 9
+    # bwd: (Q, K, V, O, dO, LSE, dQ, dK, dV, B, Hq, Hkv, N, d, scale, causal, mask, dtype,
+    #       ws, wsb, stream)
+    b = [p(0), p(1), p(2), p(3), p(4), p(5), p(6), p(7), p(8), 2, 8, 2, 128, 64, 0.125, 1, None,
+         BF16, p(9), 1 << 20, None]
+    for idx, val, code in ((11, 3, 2), (11, 0, 2), (8, None, 1), (18, None, 6),
+                           (19, 4 * 2 * 8 * 128 - 1, 6), (7, p(6, 64), 9), (17, 2, 4)):
+        bad = list(b); bad[idx] = val
+        assert lib.fa_bwd_gqa(*bad) == code, (idx, val)
 
 
 def test_decode_plan(lib):
