@@ -34,3 +34,4 @@ from .online import (  # noqa: F401
 )
 from . import decode  # noqa: F401
 from . import gqa  # noqa: F401
+from . import fp8  # noqa: F401
