@@ -135,6 +135,8 @@ def main():
     if args.workload in W.DECODE_WORKLOADS:
         return bench_decode(args)
     w = W.WORKLOADS[args.workload]
+    if w.dtype == "fp8":
+        return bench_fp8(args, w)
     x = W.make_inputs(w)
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -323,6 +325,72 @@ def cpu_baseline_decode(w, x, budget_s):
         "kind": "oracle",
         "sample": f"{len(done)} of {w.B} sequences (all heads, fp64 NumPy), {el:.1f} s",
     }
+
+
+def bench_fp8(args, w):
+    """FP8 forward: one step is one fa_fwd_fp8 call over the whole batch
+    (inputs quantized to E4M3 on the host before timing)."""
+    import torch
+    from io_aware_exact_09_amd import accounting, fa
+    from io_aware_exact_09_amd import workloads as W
+
+    x = W.make_inputs(w)
+    qz = W.quantize_fp8(x["q"], x["k"], x["v"])
+    dev = torch.device("cuda:0")
+    t = {n: torch.from_numpy(np.ascontiguousarray(qz[n])).to(dev)
+         for n in ("q8", "k8", "vt8", "sq", "sk", "sv")}
+    o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+    def step():
+        fa.fa_fwd_fp8(t["q8"], t["k8"], t["vt8"], t["sq"], t["sk"], t["sv"], o, lse, w.scale,
+                      w.causal)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record()
+        step()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [e[0].elapsed_time(e[1]) for e in evs]
+    ms_step = evs[0][0].elapsed_time(evs[-1][1]) / args.steps
+    fl = accounting.flops(w.B, w.H, w.N, w.d, w.causal, None)
+    peak = 5000.0                                   # dense FP8 MFMA, TFLOP/s
+    value = fl["fwd"] / (ms_step * 1e-3) / 1e12
+    avg = statistics.mean(per)
+    ach = fl["fwd_kernel"] / (avg * 1e-3) / 1e12
+    s = sorted(per)
+    out = {
+        "metric": "attention FP8 (E4M3) forward TFLOP/s (1 MI355X) and % of FP8 MFMA peak",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic (seeded iid normal Q, K, V quantized to E4M3 per block)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "parallelism": "none (1 GPU)"},
+        "pct_of_peak": 100.0 * value / peak,
+        "step_ms_stats": {"mean": statistics.mean(s), "p50": s[len(s) // 2],
+                          "p95": s[min(len(s) - 1, int(0.95 * len(s)))]},
+        "wall_s_timed": wall,
+        "roofline": {"kernel": "fa_fwd_fp8_kernel", "bound": "mfma", "achieved": ach,
+                     "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
+                     "traffic": recorded_traffic(w.name, "fa_fwd_fp8_kernel"),
+                     "algorithmic_flops_per_launch": fl["fwd_kernel"], "avg_launch_ms": avg},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out))
 
 
 def decode_traffic(workload, S):

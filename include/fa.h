@@ -209,6 +209,31 @@ fa_status fa_bwd_gqa(const void* Q, const void* K, const void* V, const void* O,
                      size_t workspace_bytes, void* stream);
 
 /*
+ * fa_fwd_fp8 -- attention forward on FP8 inputs, both products on the gfx950
+ * FP8 matrix cores (FlashAttention-3 runs its forward in FP8: [Training-FA],
+ * the list of versions; [Week-13], the note on FA2 and FA3).
+ *
+ * Values are OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits; largest magnitude 448) with fp32 block scales: the value of a code c
+ * of Q (K) in row block t = r / 128 of head (b, h) is E4M3(c) *
+ * q_scale[b][h][t] (k_scale), of V E4M3(c) * v_scale[b][h].  The result is
+ * attention on those values (O, LSE as for fa_fwd); the probabilities are
+ * rounded to E4M3 for the P V product (P~ = 2^8 e^(s - m) <= 256, m the
+ * running row max), the row sums are not.
+ *
+ *   Q8, K8    in : [B, H, N, d] uint8 codes
+ *   Vt8       in : [B, H, d, N] uint8 codes (V transposed); all codes finite
+ *   q_scale, k_scale in: [B, H, ceil(N/128)] fp32 (> 0);  v_scale in: [B, H] fp32
+ *   O         out: [B, H, N, d] bf16;  LSE out: [B, H, N] fp32
+ * N must be a multiple of 16 (FA_ERR_SHAPE otherwise); other checks as for
+ * fa_fwd.
+ */
+fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* Vt8, const float* q_scale,
+                     const float* k_scale, const float* v_scale, void* O, float* LSE, int B,
+                     int H, int N, int d, float scale, int causal,
+                     const unsigned char* block_mask, void* stream);
+
+/*
  * fa_decode -- attention of a few new query rows against a key/value cache,
  * with grouped key/value heads (inference decode; the week-13 page's note on
  * decode attention and GQA, snula.amonoc.com/course/ru/week-13.html).

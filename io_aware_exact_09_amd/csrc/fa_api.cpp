@@ -313,6 +313,41 @@ fa_status bwd_impl(const void* Q, const void* K, const void* V, const void* O, c
 }  // namespace
 
 // ---------------------------------------------------------------------------
+// FP8 forward
+// ---------------------------------------------------------------------------
+
+FA_EXPORT fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* Vt8,
+                               const float* q_scale, const float* k_scale,
+                               const float* v_scale, void* O, float* LSE, int B, int H, int N,
+                               int d, float scale, int causal, const unsigned char* block_mask,
+                               void* stream) {
+  FA_TRY(check_buffers({{Q8, 0, 0}, {K8, 0, 0}, {Vt8, 0, 0}, {q_scale, 0, 0}, {k_scale, 0, 0},
+                        {v_scale, 0, 0}},
+                       {{O, 0, 0}, {LSE, 0, 0}}));
+  const Shape s{B, H, N, d, FA_BF16};
+  FA_TRY(check_shape(s, scale));
+  if (N % 16) return FA_ERR_SHAPE;      // V^T rows must start on 16-byte boundaries
+  const uintptr_t cb = s.tensor_bytes() / 2, ob = s.tensor_bytes(), lb = s.row_bytes();
+  const uintptr_t T = (N + 127) / 128;
+  const uintptr_t sb = (uintptr_t)B * H * T * 4;
+  const Buf m{block_mask, block_mask ? s.mask_bytes() : 0, 1};
+  FA_TRY(check_layout({{Q8, cb, 16}, {K8, cb, 16}, {Vt8, cb, 16}, {q_scale, sb, 4},
+                       {k_scale, sb, 4}, {v_scale, (uintptr_t)B * H * 4, 4}, m},
+                      {{O, ob, 16}, {LSE, lb, 4}}, nullptr, false, 0));
+  fa::Fp8FwdArgs a{};
+  a.q = static_cast<const uint8_t*>(Q8);
+  a.k = static_cast<const uint8_t*>(K8);
+  a.vt = static_cast<const uint8_t*>(Vt8);
+  a.sq = q_scale; a.sk = k_scale; a.sv = v_scale;
+  a.o = O; a.lse = LSE; a.mask = block_mask;
+  a.BH = B * H; a.N = N; a.d = d; a.T = (int)T;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.stream = static_cast<hipStream_t>(stream);
+  return fa::launch_fwd_fp8(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+// ---------------------------------------------------------------------------
 // Decode
 // ---------------------------------------------------------------------------
 

@@ -44,7 +44,21 @@ struct BwdArgs {
   hipStream_t stream;
 };
 
+// FP8 (E4M3) forward: Q, K [BH][N][d] and V^T [BH][d][N] codes; scales sQ,
+// sK [BH][ceil(N/128)], sV [BH]; O bf16 [BH][N][d], LSE fp32 [BH][N].
+struct Fp8FwdArgs {
+  const uint8_t* q; const uint8_t* k; const uint8_t* vt;
+  const float* sq; const float* sk; const float* sv;
+  void* o; float* lse;
+  const uint8_t* mask;
+  int BH, N, d, T;
+  float scale;
+  bool causal;
+  hipStream_t stream;
+};
+
 hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_fwd_fp8(const Fp8FwdArgs& a);
 hipError_t launch_bwd_preprocess(const BwdArgs& a);
 hipError_t launch_bwd_dkdv(const BwdArgs& a);
 hipError_t launch_bwd_dq(const BwdArgs& a);

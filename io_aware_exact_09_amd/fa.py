@@ -81,6 +81,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp,
                                    i, vp, sz, vp]
         lib.fa_bwd_gqa.restype = i
+        lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp]
+        lib.fa_fwd_fp8.restype = i
         lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, sz,
                                   vp]
         lib.fa_decode.restype = i
@@ -98,7 +100,7 @@ def header_functions(path: str = HEADER_PATH) -> list[str]:
     """Names of the functions include/fa.h declares."""
     text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"\b(fa_[a-z_]+)\s*\(", text)
+    return re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)
 
 
 def status_str(status: int) -> str:
@@ -290,6 +292,27 @@ def fa_bwd_gqa(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = Fal
                         int(bool(causal)), _ptr(block_mask), _dtype_code(q), _ptr(workspace),
                         _nbytes(workspace), _stream(stream))
     _check(st, "fa_bwd_gqa")
+
+
+def fa_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, o, lse, scale: float,
+               causal: bool = False, block_mask=None, stream=None) -> None:
+    """FP8 (E4M3) forward: q8, k8 uint8 [B,H,N,d]; vt8 uint8 [B,H,d,N] (V
+    transposed); q_scale, k_scale fp32 [B,H,ceil(N/128)]; v_scale fp32 [B,H];
+    o bf16 [B,H,N,d]; lse fp32 [B,H,N]."""
+    lib = load_library()
+    _check_tensors(q8, dict(q8=q8, k8=k8, vt8=vt8, q_scale=q_scale, k_scale=k_scale,
+                            v_scale=v_scale, o=o, lse=lse))
+    _mask_ok(q8, block_mask)
+    for name, t in (("q8", q8), ("k8", k8), ("vt8", vt8)):
+        if t.dtype != torch.uint8:
+            raise TypeError(f"{name} must hold uint8 E4M3 codes")
+    if o.dtype != torch.bfloat16:
+        raise TypeError("o must be bfloat16")
+    B, H, N, d = q8.shape
+    st = lib.fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(vt8), _ptr(q_scale), _ptr(k_scale),
+                        _ptr(v_scale), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                        int(bool(causal)), _ptr(block_mask), _stream(stream))
+    _check(st, "fa_fwd_fp8")
 
 
 def fa_decode_num_splits(B, Hq, Hkv, Nq, Nkv, d, num_splits=0) -> int:

@@ -34,18 +34,22 @@ ROOT = os.path.dirname(HERE)
 PROFILES = os.path.join(ROOT, "profiles")
 
 KERNELS = ("fa_fwd_kernel", "fa_fwd_pp_kernel", "fa_bwd_delta_kernel", "fa_bwd_dkdv_kernel",
-           "fa_bwd_dq_kernel", "fa_decode_split_kernel", "fa_decode_combine_kernel")
+           "fa_bwd_dq_kernel", "fa_decode_split_kernel", "fa_decode_combine_kernel",
+           "fa_fwd_fp8_kernel")
 
 # Device sources of each kernel family (host-side files such as fa_api.cpp
 # do not change what a kernel does on the GPU).
 SOURCES = {
     "train": ("fa_common.hpp", "fa_launch.hpp", "fa_fwd.hip", "fa_bwd.hip"),
     "decode": ("fa_common.hpp", "fa_decode.hpp", "fa_decode.hip"),
+    "fp8": ("fa_common.hpp", "fa_launch.hpp", "fa_fwd_fp8.hip"),
 }
 
 
 def family(workload: str) -> str:
-    return "decode" if workload.startswith("decode") else "train"
+    if workload.startswith("decode"):
+        return "decode"
+    return "fp8" if workload.endswith("fp8") else "train"
 
 
 def source_hash(fam: str = "train") -> str:

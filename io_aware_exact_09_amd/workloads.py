@@ -17,6 +17,7 @@ The five workloads stand in for the shapes the FlashAttention reading guide
   verylong  B=1  H=8  N=16384 d=128  bf16  causal         sigma = 0.5
   long_gqa  as long (without the x20 rows), 4 key/value heads shared by
             the 16 query heads
+  long_fp8  as long, quantized to FP8 (E4M3) for the FP8 forward
 
 Recipe (the same for every workload): ``rng = numpy.random.default_rng(seed)``
 (PCG64); draw Q, K, V, dO in that order, each
@@ -86,6 +87,10 @@ WORKLOADS = {
     # key/value head, the grouping of the week-13 page's Llama-3-8B example),
     # iid N(0, 1) inputs
     "long_gqa": Workload("long_gqa", 2, 16, 4096, 128, "bf16", True, seed=1006, Hkv=4),
+    # the long-context shape as FP8 (E4M3) inputs for the FP8 forward: Q, K, V
+    # drawn as for long (x20 rows included), then quantized by quantize_fp8
+    "long_fp8": Workload("long_fp8", 2, 16, 4096, 128, "fp8", True,
+                         k_row_frac=0.01, k_row_gain=20.0, seed=1007),
 }
 
 
@@ -148,6 +153,49 @@ def make_decode_inputs(w: DecodeWorkload, seed: Optional[int] = None) -> dict:
     if w.dtype == "bf16":
         q, k, v = (bf16_round(t) for t in (q, k, v))
     return dict(q=q, k=k, v=v, seqlens=lens, scale=w.scale, causal=w.causal, dtype=w.dtype)
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """OCP E4M3 codes (uint8) of float values: round to nearest, ties to even,
+    saturating at +-448 (inputs must be finite)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    tiny = a < 2.0 ** -6
+    e = np.floor(np.log2(np.where(tiny, 1.0, a)))
+    m = np.rint(np.where(tiny, a / 2.0 ** -9, (a / np.exp2(e) - 1.0) * 8.0))   # half to even
+    carry = ~tiny & (m == 8)
+    e = np.where(carry, e + 1, e)
+    m = np.where(carry, 0, m)
+    code = np.where(tiny, m, (e + 7) * 8 + m).astype(np.int64)
+    code = np.minimum(code, 0x7E)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_fp8(q, k, v, block: int = MASK_BLOCK) -> dict:
+    """FP8 (E4M3) inputs of the FP8 forward: Q and K with one fp32 scale per
+    (batch, head, 128-row block), V with one per (batch, head), scale =
+    amax / 448 (1 for an all-zero block); V's codes transposed to [B, H, d, N]."""
+    def rows(x):
+        B, H, N, d = x.shape
+        nb = -(-N // block)
+        codes = np.empty(x.shape, np.uint8)
+        sc = np.empty((B, H, nb), np.float32)
+        for t in range(nb):
+            blk = x[:, :, t * block:(t + 1) * block].astype(np.float64)
+            amax = np.abs(blk).max(axis=(2, 3))
+            s = np.where(amax > 0, amax / 448.0, 1.0).astype(np.float32)
+            sc[:, :, t] = s
+            codes[:, :, t * block:(t + 1) * block] = e4m3_encode(
+                blk / s.astype(np.float64)[:, :, None, None])
+        return codes, sc
+    q8, sq = rows(q)
+    k8, sk = rows(k)
+    v64 = np.asarray(v, np.float64)
+    amax = np.abs(v64).max(axis=(2, 3))
+    sv = np.where(amax > 0, amax / 448.0, 1.0).astype(np.float32)
+    vt8 = np.ascontiguousarray(e4m3_encode(v64 / sv.astype(np.float64)[:, :, None, None])
+                               .transpose(0, 1, 3, 2))
+    return dict(q8=q8, k8=k8, vt8=vt8, sq=sq, sk=sk, sv=sv)
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:

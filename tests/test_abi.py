@@ -32,7 +32,7 @@ def test_header_symbols_are_exported(lib):
     assert set(names) == {"fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
                           "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
                           "fa_fwd_dropout", "fa_bwd_dropout", "fa_decode", "fa_fwd_gqa",
-                          "fa_bwd_gqa",
+                          "fa_bwd_gqa", "fa_fwd_fp8",
                           "fa_decode_num_splits", "fa_decode_workspace_bytes"}
     out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -156,6 +156,16 @@ def test_gqa_validation(lib):
                            (19, 4 * 2 * 8 * 128 - 1, 6), (7, p(6, 64), 9), (17, 2, 4)):
         bad = list(b); bad[idx] = val
         assert lib.fa_bwd_gqa(*bad) == code, (idx, val)
+
+
+def test_fp8_validation(lib):
+    # (Q8, K8, Vt8, sq, sk, sv, O, LSE, B, H, N, d, scale, causal, mask, stream)
+    f = [p(0), p(1), p(2), p(3), p(4), p(5), p(6), p(7), 2, 4, 256, 128, 0.1, 1, None, None]
+    for idx, val, code in ((0, None, 1), (4, None, 1), (7, None, 1), (10, 250, 2), (10, 0, 2),
+                           (11, 96, 3), (12, float("nan"), 8), (2, p(2, 4), 5),
+                           (3, p(3, 2), 5), (6, p(0, 64), 9), (7, p(5), 9)):
+        bad = list(f); bad[idx] = val
+        assert lib.fa_fwd_fp8(*bad) == code, (idx, val)
 
 
 def test_decode_plan(lib):

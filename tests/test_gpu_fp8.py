@@ -1,0 +1,110 @@
+"""GPU parity of fa_fwd_fp8 (FP8 E4M3 forward) against the FP8 oracle
+(oracle/fp8.py) on the same seeded, quantized inputs.
+
+The bar (derived in oracle/fp8.py, o_error_bound): the GPU rounds the
+probabilities to E4M3 before the P V product, so per element
+    |O - O_exact| <= bound (2^-4 relative on P, 2^-10 absolute below 2^-6)
+                     + 2^-8 |O_exact| (bf16 output) + 1e-6,
+with O_exact the exact attention on the dequantized inputs; LSE carries no
+FP8 rounding and meets the usual 1e-4 max(1, |LSE|).  Also reported: the
+relative Frobenius error, held to 3e-2.
+"""
+
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from io_aware_exact_09_amd import fa
+from io_aware_exact_09_amd import workloads as W
+from oracle import fp8 as OF
+from gpu_util import device, upload_mask
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device())
+
+
+def _run(qz, scale, causal, mask):
+    B, H, N, d = qz["q8"].shape
+    q8, k8, vt8 = _dev(qz["q8"]), _dev(qz["k8"]), _dev(qz["vt8"])
+    sq, sk, sv = _dev(qz["sq"]), _dev(qz["sk"]), _dev(qz["sv"])
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=device())
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=device())
+    fa.fa_fwd_fp8(q8, k8, vt8, sq, sk, sv, o, lse, scale, causal, upload_mask(mask))
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def _check(o, lse, o_ref, lse_ref, bound, label):
+    inf = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lse), inf), f"{label}: -inf pattern of LSE"
+    lerr = np.abs(lse[~inf] - lse_ref[~inf])
+    assert np.all(lerr <= 1e-4 * np.maximum(1.0, np.abs(lse_ref[~inf]))), \
+        f"{label}: LSE error {lerr.max():.3e}"
+    assert np.isfinite(o).all()
+    err = np.abs(o - o_ref)
+    lim = bound + 2.0 ** -8 * np.abs(o_ref) + 1e-6
+    worst = float((err / lim).max())
+    rel = float(np.linalg.norm(o - o_ref) / max(np.linalg.norm(o_ref), 1e-30))
+    _say(f"  {label}: O max|err|={err.max():.3e} (worst err/bound {worst:.3f}) "
+         f"rel-Frobenius {rel:.3e}; LSE max|err|={lerr.max() if lerr.size else 0:.3e}")
+    assert worst <= 1.0, f"{label}: O outside the FP8 bound (ratio {worst:.3f})"
+    assert rel <= 3e-2, f"{label}: O rel-Frobenius {rel:.3e}"
+
+
+SMALL = [
+    # (B, H, N, d, causal, mask)
+    (1, 2, 128, 64, False, None),
+    (2, 2, 272, 128, True, None),
+    (1, 3, 400, 64, True, "rand"),
+    (2, 1, 1024, 128, False, None),
+    (1, 2, 16, 128, True, None),
+    (1, 2, 528, 128, False, "rand"),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,mk", SMALL,
+                         ids=[f"B{a}-H{b}-N{c}-d{e}-{'causal' if f else 'dense'}-{g or 'nomask'}"
+                              for a, b, c, e, f, g in SMALL])
+def test_small_against_oracle(B, H, N, d, causal, mk):
+    rng = np.random.default_rng(N + d)
+    q, k, v = (rng.standard_normal((B, H, N, d)).astype(np.float32) for _ in range(3))
+    k[:, :, ::37] *= 8.0                       # some large logits
+    mask = W.random_block_mask(N, 0.6, seed=N) if mk == "rand" else None
+    qz = W.quantize_fp8(q, k, v)
+    scale = 1.0 / math.sqrt(d)
+    _say(f"case B={B} H={H} N={N} d={d} causal={causal} mask={mk}")
+    o, lse = _run(qz, scale, causal, mask)
+    args = (qz["q8"], qz["k8"], qz["vt8"], qz["sq"], qz["sk"], qz["sv"], scale, causal, mask)
+    o_ref, lse_ref = OF.forward(*args)
+    bound = OF.o_error_bound(*args)
+    _check(o, lse, o_ref, lse_ref, bound, "whole output")
+
+
+def test_full_size_long_fp8_sampled():
+    """The long-context shape (B=2, H=16, N=4096, d=128, causal, 1% of K rows
+    x20) quantized to FP8, as the benchmark runs it; sampled rows of three
+    heads against the oracle."""
+    w = W.WORKLOADS["long_fp8"]
+    x = W.make_inputs(w)
+    qz = W.quantize_fp8(x["q"], x["k"], x["v"])
+    _say(f"workload long_fp8: B={w.B} H={w.H} N={w.N} d={w.d}")
+    o, lse = _run(qz, w.scale, w.causal, None)
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, w.N // 2, w.N - 1],
+                                     rng.choice(w.N, size=40, replace=False)]))
+    for b, h in ((0, 0), (1, 15), (0, 9)):
+        r = OF.head_rows(qz["q8"], qz["k8"], qz["vt8"], qz["sq"], qz["sk"], qz["sv"], b, h,
+                         rows, w.scale, w.causal)
+        _check(o[b, h][rows], lse[b, h][rows], r["O"], r["LSE"], r["bound"], f"head ({b},{h})")
