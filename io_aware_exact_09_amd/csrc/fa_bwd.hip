@@ -215,9 +215,40 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
           dpv = E::mma(ao[t], vf[t0 + t], dpv);
         }
       };
+      // Dropout keep bits of query half qh: bit r for register r (query
+      // 32qh + 8(r/4) + 4g + r%4, key krow).  A Philox call yields the words of
+      // four consecutive keys, i.e. of the four lanes of a lane quad, so lane
+      // m of the quad draws the calls of registers 4m..4m+3 for the whole quad
+      // and the quad exchanges the 16 keep bits each lane drew (DPP
+      // broadcasts): 4 calls per lane instead of 16.
+      uint32_t kbits[NQH];
+      auto drop_bits = [&](int qh) -> uint32_t {
+        const int m = l32 & 3;
+        uint32_t mine = 0;      // bit 4x + k: call of register 4m + x, key of quad lane k
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const Philox4 z = philox4x32_10((uint32_t)krow >> 2,
+                                          (uint32_t)(q0 + 32 * qh + 8 * m + 4 * g + x),
+                                          (uint32_t)bhq, 0u, drp.key0, drp.key1);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) mine |= (uint32_t)(z.w[k] >= drp.thresh) << (4 * x + k);
+        }
+        // this lane's bits (k = m) of quad lane src's draws -> registers 4src..4src+3
+        auto mine_of = [&](auto src_tag) {
+          constexpr int src = decltype(src_tag)::value;
+          const uint32_t v =
+              (uint32_t)__builtin_amdgcn_mov_dpp((int)mine, src * 0x55, 0xF, 0xF, true) >> m;
+          return ((v & 1u) | ((v >> 3) & 2u) | ((v >> 6) & 4u) | ((v >> 9) & 8u)) << (4 * src);
+        };
+        return mine_of(IntTag<0>{}) | mine_of(IntTag<1>{}) | mine_of(IntTag<2>{}) |
+               mine_of(IntTag<3>{});
+      };
       // P = 2^(S c - LSE log2 e), dS = P (dP - D) for register groups
       // a0 .. a1-1 (register r holds query 32qh + 8(r/4) + 4g + r%4).
       auto pds_part = [&](int qh, int a0, int a1, f32x16& sv, f32x16& dpv) {
+        if constexpr (DROP) {
+          if (a0 == 0) kbits[qh] = drop_bits(qh);
+        }
 #pragma unroll
         for (int a = a0; a < a1; ++a) {
           const int qi = 32 * qh + 8 * a + 4 * g;
@@ -231,11 +262,7 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
             if constexpr (DROP) {
               // dV takes the dropped probabilities (its 1/(1-p) is applied at
               // the end); dS = P (dP M - D) with M = Z / (1-p).
-              const Philox4 z = philox4x32_10((uint32_t)krow >> 2, (uint32_t)(q0 + qi + x),
-                                              (uint32_t)bhq, 0u, drp.key0, drp.key1);
-              const uint32_t word = (krow & 2) ? ((krow & 1) ? z.w[3] : z.w[2])
-                                               : ((krow & 1) ? z.w[1] : z.w[0]);
-              const bool keep = word >= drp.thresh;
+              const bool keep = (kbits[qh] >> r) & 1u;
               sv[r] = keep ? p : 0.f;
               dpv[r] = p * (keep ? fmaf(dpv[r], drp.inv_keep, -dv[x]) : -dv[x]);
             } else {
