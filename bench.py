@@ -83,6 +83,21 @@ def recorded_traffic(workload, kernel):
     return k["read_bytes"] + k["write_bytes"]
 
 
+def copy_probe(args, dev):
+    """With --copy-probe: one torch.neg over FA_COPY_PROBE_BYTES (512 MiB) of
+    bf16, reading n bytes and writing n bytes, to calibrate the rocprofv3
+    FETCH_SIZE / WRITE_SIZE counters (the probe is found by its kernel name)."""
+    if not args.copy_probe:
+        return
+    import torch
+    n = int(os.environ.get("FA_COPY_PROBE_BYTES", 512 << 20))
+    src = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def cpu_baseline(w, x, budget_s):
     """Time the fp64 oracle (fwd + bwd, whole heads) on a bounded sample."""
     import oracle
@@ -149,13 +164,7 @@ def main():
     ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8,
                      device=dev)
     sc, cz = w.scale, w.causal
-    if args.copy_probe:
-        n = int(os.environ.get("FA_COPY_PROBE_BYTES", 512 << 20))
-        src = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
-        dst = torch.empty_like(src)
-        torch.neg(src, out=dst)            # reads n bytes, writes n bytes
-        torch.cuda.synchronize()
-        del src, dst
+    copy_probe(args, dev)
 
     drop = args.dropout
     grouped = w.Hkv is not None and w.Hkv != w.H
@@ -341,6 +350,7 @@ def bench_fp8(args, w):
          for n in ("q8", "k8", "vt8", "sq", "sk", "sv")}
     o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    copy_probe(args, dev)
 
     def step():
         fa.fa_fwd_fp8(t["q8"], t["k8"], t["vt8"], t["sq"], t["sk"], t["sv"], o, lse, w.scale,
@@ -420,13 +430,7 @@ def bench_decode(args):
     S = fa.fa_decode_num_splits(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.d)
     nws = fa.fa_decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.d)
     ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
-    if args.copy_probe:
-        n = int(os.environ.get("FA_COPY_PROBE_BYTES", 512 << 20))
-        src = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
-        dst = torch.empty_like(src)
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_probe(args, dev)
 
     def step():
         fa.fa_decode(q, k, v, o, lse, w.scale, sl, w.causal, 0, ws)
