@@ -161,8 +161,8 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.empty(fa.fa_bwd_gqa_workspace_bytes(w.B, w.H, w.kv_heads, w.N, w.d),
+                     dtype=torch.uint8, device=dev)
     sc, cz = w.scale, w.causal
     copy_probe(args, dev)
 

@@ -194,11 +194,19 @@ fa_status fa_bwd_dropout(const void* Q, const void* K, const void* V, const void
  *
  *   Q, O, dO, dQ : [B, Hq, N, d] dtype;  LSE: [B, Hq, N] fp32
  *   K, V, dK, dV : [B, Hkv, N, d] dtype (dK, dV overwritten)
- *   workspace    : at least fa_bwd_workspace_bytes(B, Hq, N, d) bytes
+ *   workspace    : at least fa_bwd_gqa_workspace_bytes(B, Hq, Hkv, N, d) bytes
  * Hq must be a multiple of Hkv (FA_ERR_SHAPE otherwise); other arguments and
  * checks as for fa_fwd / fa_bwd (with H = Hq).  Hkv = Hq gives exactly
- * fa_fwd / fa_bwd.
+ * fa_fwd / fa_bwd.  When B * Hkv * ceil(N/128) is small (under 512 work-groups)
+ * a group's query heads are divided among up to G work-groups that each write
+ * an fp32 partial dK, dV into the workspace, and a fourth kernel adds the
+ * partials in a fixed order (still deterministic).
+ *
+ * fa_bwd_gqa_workspace_bytes: 4 * B * Hq * N bytes for D, plus, when the dK/dV
+ * work is divided, 2 * splits * B * Hkv * N * d * 4 bytes of partials; 0 for
+ * sizes fa_bwd_gqa would reject.
  */
+size_t fa_bwd_gqa_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
 fa_status fa_fwd_gqa(const void* Q, const void* K, const void* V, void* O, float* LSE,
                      int B, int Hq, int Hkv, int N, int d, float scale, int causal,
                      const unsigned char* block_mask, fa_dtype dtype, void* stream);

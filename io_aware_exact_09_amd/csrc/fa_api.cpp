@@ -127,6 +127,28 @@ fa_status check_kv_heads(int H, int Hkv) {
   return FA_OK;
 }
 
+// Work-groups per key/value head and key block in the grouped dK/dV pass:
+// with fewer than two work-groups per compute unit (about 512 on the 256-CU
+// MI355X) the group's query heads are divided among several work-groups.
+int gqa_split(int B, int H, int Hkv, int N) {
+  const int G = H / Hkv;
+  if (G <= 1) return 1;
+  const long long groups = (long long)B * Hkv * ((N + 127) / 128);
+  if (groups >= 512) return 1;
+  return (int)std::min<long long>(G, (512 + groups - 1) / groups);
+}
+
+// Backward workspace: D (4 bytes per query row), then, when the grouped
+// dK/dV pass is split, its fp32 partials.
+size_t bwd_workspace(const Shape& s, int Hkv, int* gsplit, size_t* part_off) {
+  const int sp = gqa_split(s.B, s.H, Hkv, s.N);
+  const size_t rows = ((size_t)s.row_bytes() + 255) / 256 * 256;
+  if (gsplit) *gsplit = sp;
+  if (part_off) *part_off = rows;
+  if (sp == 1) return (size_t)s.row_bytes();
+  return rows + (size_t)2 * sp * s.B * Hkv * s.N * s.d * 4;
+}
+
 }  // namespace
 
 FA_EXPORT fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
@@ -262,6 +284,12 @@ FA_EXPORT fa_status fa_bwd_dropout(const void* Q, const void* K, const void* V, 
                   dtype, workspace, workspace_bytes, drop, stream);
 }
 
+FA_EXPORT size_t fa_bwd_gqa_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
+  const Shape s{B, Hq, N, d, FA_BF16};
+  if (check_shape(s, 1.0f) != FA_OK || check_kv_heads(Hq, Hkv) != FA_OK) return 0;
+  return bwd_workspace(s, Hkv, nullptr, nullptr);
+}
+
 FA_EXPORT fa_status fa_fwd_gqa(const void* Q, const void* K, const void* V, void* O, float* LSE,
                                int B, int Hq, int Hkv, int N, int d, float scale, int causal,
                                const unsigned char* block_mask, fa_dtype dtype, void* stream) {
@@ -292,14 +320,19 @@ fa_status bwd_impl(const void* Q, const void* K, const void* V, const void* O, c
   FA_TRY(check_kv_heads(H, Hkv));
   const uintptr_t tb = s.tensor_bytes(), lb = s.row_bytes();
   const uintptr_t kvb = tb / H * Hkv;
+  int gsplit = 1;
+  size_t part_off = 0;
+  const size_t need = bwd_workspace(s, Hkv, &gsplit, &part_off);
   const Buf ws{workspace, workspace_bytes, 16};
   const Buf m{block_mask, block_mask ? s.mask_bytes() : 0, 1};
   FA_TRY(check_layout(
       {{Q, tb, 16}, {K, kvb, 16}, {V, kvb, 16}, {O, tb, 16}, {dO, tb, 16}, {LSE, lb, 4}, m},
-      {{dQ, tb, 16}, {dK, kvb, 16}, {dV, kvb, 16}}, &ws, true, lb));
+      {{dQ, tb, 16}, {dK, kvb, 16}, {dV, kvb, 16}}, &ws, true, need));
 
   fa::BwdArgs a = bwd_args(s, scale, causal, block_mask, stream);
   a.G = H / Hkv;
+  a.gsplit = gsplit;
+  if (gsplit > 1) a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_off);
   a.q = Q; a.k = K; a.v = V; a.o = O; a.dout = dO; a.lse = LSE;
   a.dq = dQ; a.dk = dK; a.dv = dV;
   a.delta = static_cast<float*>(workspace);

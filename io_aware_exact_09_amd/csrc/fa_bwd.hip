@@ -23,6 +23,8 @@
 // Splitting dQ into its own pass recomputes S and dP once more but needs no
 // atomics, so the result is deterministic.
 
+#include <algorithm>
+
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -78,6 +80,7 @@ __attribute__((amdgpu_waves_per_eu(1, 1)))
 fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                    const T* __restrict__ dO, const float* __restrict__ LSE,
                    const float* __restrict__ delta, T* __restrict__ dK, T* __restrict__ dV,
+                   float* __restrict__ part, int gsplit,
                    const uint8_t* __restrict__ mask, int BH, int kv_group, int N, int T_tiles,
                    float c, float scale, DropParams drp) {
   using E = Elem<T>;
@@ -100,10 +103,14 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
   const int nkb = (N + BK - 1) / BK;
-  // BH counts key/value heads here; query heads bh*kv_group .. +kv_group-1
-  // share head bh, and their contributions to dK, dV are summed on chip.
+  // BH counts (key/value head, split) pairs here: query heads
+  // bh*kv_group .. +kv_group-1 share head bh, and their contributions to dK,
+  // dV are summed on chip.  With gsplit > 1 the group's query heads are
+  // divided among gsplit work-groups (more work-groups when there are few key
+  // blocks), each writing an fp32 partial that a reduction kernel adds up.
   const BlockCoord bc = map_block(blockIdx.x, nkb, BH, CAUSAL, false);
-  const int bh = bc.bh, kb = bc.blk, k0 = kb * BK;
+  const int bh = bc.bh / gsplit, sp = bc.bh - bh * gsplit;
+  const int kb = bc.blk, k0 = kb * BK;
   const size_t head = (size_t)bh * N * D;   // K, V, dK, dV of this key/value head
   const int kw = k0 + 32 * w;            // this wave's first key
   const int krow = kw + l32;             // this lane's key
@@ -135,7 +142,8 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
 
   // The walk covers (query head of the group, staged tile) pairs u =
   // gq * ntiles + i, kept tiles only.
-  const int NU = kv_group * ntiles;
+  const int U0 = (sp * kv_group / gsplit) * ntiles;
+  const int NU = ((sp + 1) * kv_group / gsplit) * ntiles;
   auto next_u = [&](int u) {
     while (u < NU) {
       const int gq = u / ntiles;
@@ -400,7 +408,7 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
     }
   };
 
-  int u = next_u(0);
+  int u = next_u(U0);
   if (u < NU) stage(u, IntTag<0>{});
   if constexpr (sizeof(T) == 2) {
     // Two iterations per trip with the buffer index a compile-time constant,
@@ -425,6 +433,27 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   }
 
   // dV^T / dK^T C layout: lane (key l32, g), register r -> d = 32b + 8(r/4) + 4g + r%4.
+  if (gsplit > 1) {
+    if (krow < N) {
+      const size_t E = (size_t)(BH / gsplit) * N * D;     // elements of dK
+      float* pk = part + (size_t)sp * E + head + (size_t)krow * D;
+      float* pv = part + (size_t)(gsplit + sp) * E + head + (size_t)krow * D;
+      const float vs = DROP ? drp.inv_keep : 1.0f;
+#pragma unroll
+      for (int b = 0; b < ND; ++b)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int d0 = 32 * b + 8 * a + 4 * g;
+          *reinterpret_cast<f32x4*>(pv + d0) =
+              f32x4{dvacc[b][4 * a], dvacc[b][4 * a + 1], dvacc[b][4 * a + 2],
+                    dvacc[b][4 * a + 3]} * vs;
+          *reinterpret_cast<f32x4*>(pk + d0) =
+              f32x4{dkacc[b][4 * a], dkacc[b][4 * a + 1], dkacc[b][4 * a + 2],
+                    dkacc[b][4 * a + 3]} * scale;
+        }
+    }
+    return;
+  }
   if (krow < N) {
     T* dKr = dK + head + (size_t)krow * D;
     T* dVr = dV + head + (size_t)krow * D;
@@ -439,6 +468,25 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
         E::store4(dKr + d0, dkacc[b][4 * a] * scale, dkacc[b][4 * a + 1] * scale,
                   dkacc[b][4 * a + 2] * scale, dkacc[b][4 * a + 3] * scale);
       }
+  }
+}
+
+// dK, dV = the sum of the gsplit fp32 partials of the dK/dV pass (element
+// order of dK; partials laid out [2][gsplit][E], dK first).
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+fa_bwd_dkdv_reduce_kernel(const float* __restrict__ part, T* __restrict__ dK,
+                          T* __restrict__ dV, size_t E4 /* elements / 4 */, int gsplit) {
+  const f32x4* p = reinterpret_cast<const f32x4*>(part);
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < E4;
+       i += (size_t)gridDim.x * blockDim.x) {
+    f32x4 k = f32x4{}, v = f32x4{};
+    for (int sp = 0; sp < gsplit; ++sp) {
+      k += p[(size_t)sp * E4 + i];
+      v += p[(size_t)(gsplit + sp) * E4 + i];
+    }
+    Elem<T>::store4(dK + 4 * i, k[0], k[1], k[2], k[3]);
+    Elem<T>::store4(dV + 4 * i, v[0], v[1], v[2], v[3]);
   }
 }
 
@@ -684,15 +732,22 @@ template <typename T, int D, bool CAUSAL, bool MASKED>
 static hipError_t launch_dkdv_t(const BwdArgs& a) {
   const int nkb = (a.N + DkdvCfg<T>::BK - 1) / DkdvCfg<T>::BK;
   auto go = [&](auto kernel) {
-    const int bh_kv = a.BH / a.G;     // one work-group row per key/value head
-    hipLaunchKernelGGL(kernel, dim3(nkb * bh_kv), dim3(kThreads), 0, a.stream,
+    // one work-group row per (key/value head, split of its query heads)
+    const int rows = a.BH / a.G * a.gsplit;
+    hipLaunchKernelGGL(kernel, dim3(nkb * rows), dim3(kThreads), 0, a.stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
-                       static_cast<T*>(a.dk), static_cast<T*>(a.dv), a.mask, bh_kv, a.G, a.N,
-                       a.T, score_coef(a.scale), a.scale, drop_params(a));
+                       static_cast<T*>(a.dk), static_cast<T*>(a.dv), a.part, a.gsplit, a.mask,
+                       rows, a.G, a.N, a.T, score_coef(a.scale), a.scale, drop_params(a));
   };
   if (a.drop.on) go(fa_bwd_dkdv_kernel<T, D, CAUSAL, MASKED, true>);
   else go(fa_bwd_dkdv_kernel<T, D, CAUSAL, MASKED, false>);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.gsplit == 1) return e;
+  const size_t E4 = (size_t)(a.BH / a.G) * a.N * D / 4;
+  const unsigned blocks = (unsigned)std::min<size_t>((E4 + kThreads - 1) / kThreads, 4096);
+  hipLaunchKernelGGL((fa_bwd_dkdv_reduce_kernel<T>), dim3(blocks), dim3(kThreads), 0, a.stream,
+                     a.part, static_cast<T*>(a.dk), static_cast<T*>(a.dv), E4, a.gsplit);
   return hipGetLastError();
 }
 

@@ -38,6 +38,8 @@ struct BwdArgs {
   const uint8_t* mask;
   int BH, N, d, T;         // BH = B * (query heads)
   int G = 1;               // query heads per key/value head (K, V, dK, dV have BH / G heads)
+  int gsplit = 1;          // work-groups sharing one key/value head's query heads in dK/dV
+  float* part = nullptr;   // fp32 dK, dV partials, [2][gsplit][BH / G * N * d] (gsplit > 1)
   float scale;
   bool causal, bf16;
   Dropout drop;

@@ -76,6 +76,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp,
                                        f, u64, i, vp, sz, vp]
         lib.fa_bwd_dropout.restype = i
+        lib.fa_bwd_gqa_workspace_bytes.argtypes = [i, i, i, i, i]
+        lib.fa_bwd_gqa_workspace_bytes.restype = sz
         lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp]
         lib.fa_fwd_gqa.restype = i
         lib.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp,
@@ -264,6 +266,10 @@ def fa_bwd_dq(q, k, v, do, lse, dq, scale, causal=False, block_mask=None, worksp
     _check(st, "fa_bwd_dq")
 
 
+def fa_bwd_gqa_workspace_bytes(B: int, Hq: int, Hkv: int, N: int, d: int) -> int:
+    return int(load_library().fa_bwd_gqa_workspace_bytes(B, Hq, Hkv, N, d))
+
+
 def fa_fwd_gqa(q, k, v, o, lse, scale: float, causal: bool = False, block_mask=None,
                stream=None) -> None:
     """Forward with grouped key/value heads: q, o [B,Hq,N,d]; k, v [B,Hkv,N,d]."""
@@ -285,8 +291,8 @@ def fa_bwd_gqa(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = Fal
     _mask_ok(q, block_mask)
     B, Hq, N, d = q.shape
     if workspace is None:
-        workspace = torch.empty(max(fa_bwd_workspace_bytes(B, Hq, N, d), 1), dtype=torch.uint8,
-                                device=q.device)
+        need = int(lib.fa_bwd_gqa_workspace_bytes(B, Hq, k.shape[1], N, d))
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     st = lib.fa_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
                         _ptr(dk), _ptr(dv), B, Hq, k.shape[1], N, d, float(scale),
                         int(bool(causal)), _ptr(block_mask), _dtype_code(q), _ptr(workspace),

@@ -32,7 +32,7 @@ def test_header_symbols_are_exported(lib):
     assert set(names) == {"fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
                           "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
                           "fa_fwd_dropout", "fa_bwd_dropout", "fa_decode", "fa_fwd_gqa",
-                          "fa_bwd_gqa", "fa_fwd_fp8",
+                          "fa_bwd_gqa", "fa_fwd_fp8", "fa_bwd_gqa_workspace_bytes",
                           "fa_decode_num_splits", "fa_decode_workspace_bytes"}
     out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -137,6 +137,19 @@ def test_dropout_entry_points_check_like_the_plain_ones(lib, kw, code):
     assert bwd_drop(lib, **bkw) == code
 
 
+def test_gqa_workspace_bytes(lib):
+    # long_gqa: 2 x 4 key/value heads x 32 key blocks = 256 work-groups -> split in two
+    d_bytes = 4 * 2 * 16 * 4096
+    parts = 2 * 2 * 2 * 4 * 4096 * 128 * 4
+    assert fa.fa_bwd_gqa_workspace_bytes(2, 16, 4, 4096, 128) == d_bytes + parts
+    # one key/value head per query head, or enough work-groups: D only
+    assert fa.fa_bwd_gqa_workspace_bytes(2, 16, 16, 4096, 128) == d_bytes
+    assert fa.fa_bwd_gqa_workspace_bytes(16, 16, 4, 4096, 128) == 4 * 16 * 16 * 4096
+    # split capped at the group size (MQA of 4 heads, one key block)
+    assert fa.fa_bwd_gqa_workspace_bytes(1, 4, 1, 100, 64) == 1792 + 2 * 4 * 100 * 64 * 4
+    assert fa.fa_bwd_gqa_workspace_bytes(1, 6, 4, 100, 64) == 0
+
+
 def test_gqa_validation(lib):
     # fwd: (Q, K, V, O, LSE, B, Hq, Hkv, N, d, scale, causal, mask, dtype, stream)
     f = [p(0), p(1), p(2), p(3), p(4), 2, 8, 2, 128, 64, 0.125, 1, None, BF16, None]
@@ -151,9 +164,10 @@ def test_gqa_validation(lib):
     # bwd: (Q, K, V, O, dO, LSE, dQ, dK, dV, B, Hq, Hkv, N, d, scale, causal, mask, dtype,
     #       ws, wsb, stream)
     b = [p(0), p(1), p(2), p(3), p(4), p(5), p(6), p(7), p(8), 2, 8, 2, 128, 64, 0.125, 1, None,
-         BF16, p(9), 1 << 20, None]
+         BF16, p(9), 4 << 20, None]
+    need = fa.fa_bwd_gqa_workspace_bytes(2, 8, 2, 128, 64)
     for idx, val, code in ((11, 3, 2), (11, 0, 2), (8, None, 1), (18, None, 6),
-                           (19, 4 * 2 * 8 * 128 - 1, 6), (7, p(6, 64), 9), (17, 2, 4)):
+                           (19, need - 1, 6), (7, p(6, 64), 9), (17, 2, 4)):
         bad = list(b); bad[idx] = val
         assert lib.fa_bwd_gqa(*bad) == code, (idx, val)
 
