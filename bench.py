@@ -98,6 +98,24 @@ def copy_probe(args, dev):
     del src, dst
 
 
+def cold_cache_steps(step, n, dev):
+    """Secondary measurement: n more steps, each preceded (outside its event
+    pair) by a 512 MiB write that evicts the L2 caches and the 256 MB
+    Infinity Cache, so the step starts with its inputs in HBM only.  Returns
+    the per-step milliseconds."""
+    import torch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+    for i in range(n):
+        flush.fill_(i & 0xFF)
+        evs[i][0].record()
+        step()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    del flush
+    return [e[0].elapsed_time(e[1]) for e in evs]
+
+
 def cpu_baseline(w, x, budget_s):
     """Time the fp64 oracle (fwd + bwd, whole heads) on a bounded sample."""
     import oracle
@@ -212,6 +230,7 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    cold = cold_cache_steps(step, min(args.steps, 20), dev)
 
     per = {p: [e[i].elapsed_time(e[i + 1]) for e in evs] for i, p in enumerate(phases)}
     steps_ms = [e[0].elapsed_time(e[nev - 1]) for e in evs]
@@ -299,6 +318,9 @@ def main():
         "kernels": kernels,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "cold_cache": {"ms_per_step_median": statistics.median(cold),
+                       "value": total / (statistics.median(cold) * 1e-3) / 1e12,
+                       "steps": len(cold), "flush_bytes": 512 << 20},
         "peak_tflops": peak,
     }
     print(json.dumps(out))
