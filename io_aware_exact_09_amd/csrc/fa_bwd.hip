@@ -631,18 +631,24 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
             const int r = 4 * a + x;
-            float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
-            if (MASKED_TILE && 8 * a + x >= lim) p = 0.f;
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
             dp[r] = p * (z.w[x] >= drp.thresh ? fmaf(dp[r], drp.inv_keep, -dval) : -dval);
           }
         }
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
-          if (MASKED_TILE && 8 * (r >> 2) + (r & 3) >= lim) p = 0.f;
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
           dp[r] = p * (dp[r] - dval);
         }
+      }
+      // Keys this row does not keep get dS = 0 (a select, so an overflowed P
+      // of a masked key leaves nothing behind).  The flag is uniform over the
+      // wave, so tiles off the diagonal branch past this.
+      if (__builtin_expect(MASKED_TILE, 0)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + (r & 3) >= lim) dp[r] = 0.f;
       }
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
