@@ -567,16 +567,12 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
 #pragma unroll
   for (int b = 0; b < ND; ++b) dqacc[b] = f32x16{};
 
-  // Precomputed operand offsets when the register budget of two waves per
-  // SIMD allows it (bf16, d = 64); otherwise addresses are formed per read.
-  // bf16, d = 64 also takes compile-time LDS buffers (loop unrolled by two).
-  // d = 128 has no register room for either at two waves per SIMD.
-  constexpr bool USE_LO = sizeof(T) == 2 && D == 64;
-  constexpr bool USE_XO = sizeof(T) == 2 && D == 128;
+  // bf16: precomputed per-lane operand offsets and compile-time LDS buffers
+  // (loop unrolled by two), so every LDS read is a lane offset plus an
+  // immediate.  fp32 forms addresses per read (register budget).
+  constexpr bool USE_LO = sizeof(T) == 2;
   LaneOffsets<T, D> lo;
   if constexpr (USE_LO) lo.init(lane);
-  XorOffsets<__bf16, D> xo;
-  if constexpr (USE_XO) xo.init(lane);
   int j = next_kept(0);
   if (j < ntiles) stage(j, IntTag<0>{});
   wait_global_loads();
@@ -590,7 +586,6 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
     const int BUF = buf_sel;
     const unsigned char* sK = pick(buf_sel, lds0, lds1);
     const unsigned char* sV = sK + TB;
-    if constexpr (USE_XO) xo.refresh();
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       // Operands in sub-batches of SB chunks (register budget of two waves
@@ -602,9 +597,8 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
         frag ak[SB], av[SB];
 #pragma unroll
         for (int t = 0; t < SB; ++t) {
-          if constexpr (USE_LO || USE_XO) {
-            const unsigned char* p =
-                sK + (USE_LO ? lo.row[t0 + t] : xo.row_at(t0 + t)) + 32 * h * RB;
+          if constexpr (USE_LO) {
+            const unsigned char* p = sK + lo.row[t0 + t] + 32 * h * RB;
             ak[t] = row_frag_at<T>(p);
             av[t] = row_frag_at<T>(p + TB);
           } else {
@@ -659,8 +653,6 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
         for (int b = 0; b < ND; ++b) {
           if constexpr (USE_LO)
             kt[b] = trans_frag_at(sK + lo.tr[b][0] + 16 * cc * RB, sK + lo.tr[b][1] + 16 * cc * RB);
-          else if constexpr (USE_XO)
-            kt[b] = trans_frag_at(sK + xo.tr_at(b, 0) + 16 * cc * RB, sK + xo.tr_at(b, 1) + 16 * cc * RB);
           else
             kt[b] = trans_frag<T, D>(sK, b, cc, lane);
         }
@@ -677,7 +669,7 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
     const int kv0 = j * BC;
     if (jn < ntiles) stage(jn, other(buf_sel));
     const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > q0 + 32 * w);
-    if constexpr (sizeof(T) == 2 && D == 64) {
+    if constexpr (sizeof(T) == 2) {
       // Separate masked / unmasked bodies where the registers allow it.
       if (need_mask) tile(BoolTag<true>{}, buf_sel, kv0);
       else tile(BoolTag<false>{}, buf_sel, kv0);
@@ -685,7 +677,7 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
       tile(need_mask, buf_sel, kv0);
     }
   };
-  if constexpr (sizeof(T) == 2 && D == 64) {
+  if constexpr (sizeof(T) == 2) {
     while (j < ntiles) {   // two tiles per trip, buffer index compile-time
       int jn = next_kept(j + 1);
       step(IntTag<0>{}, j, jn);

@@ -371,38 +371,6 @@ struct LaneOffsets {
   }
 };
 
-// The same offsets for bf16 tiles from three per-lane bases, one XOR away:
-// the swizzle permutes 16-byte chunks only within a row, and the chunk index
-// of a read splits into a part fixed per lane and a part that only the loop
-// index sets (bits no other term of the offset touches), so
-//   natural read, chunk 2t+g of row l32:       row ^ (32 t)
-//   transposed read, block b, row group h:     tr[h] ^ (64 b)
-// with rows +32 / +16 cc added as immediates.  For kernels whose register
-// budget has no room for the full offset table: `refresh()` at the top of
-// each tile keeps the compiler from hoisting the XORs out of the loop into
-// registers.
-template <typename T, int D>
-struct XorOffsets {
-  static_assert(sizeof(T) == 2, "bf16 only");
-  uint32_t row, tr[2];
-
-  __device__ void init(int lane) {
-    using L = Tile<T, D>;
-    const int l32 = lane & 31, g = lane >> 5;
-    row = (uint32_t)(l32 * L::RB + ((g ^ L::swz(l32)) << 4));
-    const int q = lane >> 4, j = lane & 15;
-    const int x = 2 * (q & 1) + ((j & 3) >> 1);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = 4 * (q >> 1) + (j >> 2) + 8 * h;
-      tr[h] = (uint32_t)(r * L::RB + ((x ^ L::swz(r)) << 4) + 8 * (j & 1));
-    }
-  }
-  __device__ void refresh() { asm volatile("" : "+v"(row), "+v"(tr[0]), "+v"(tr[1])); }
-  __device__ uint32_t row_at(int t) const { return row ^ (uint32_t)(32 * t); }
-  __device__ uint32_t tr_at(int b, int h) const { return tr[h] ^ (uint32_t)(64 * b); }
-};
-
 // Natural-order bf16 operand at a precomputed lane offset (see row_frag).
 // (fp32 operands span two swizzled chunks and use row_frag.)
 template <typename T>
