@@ -212,15 +212,16 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
             aq[t] = row_frag<T, D>(sQ, 32 * qh + l32, t0 + t, g);
             ao[t] = row_frag<T, D>(sdO, 32 * qh + l32, t0 + t, g);
           }
-          to_agpr(aq[t]);
-          to_agpr(ao[t]);
         }
       };
       auto sdp_mma = [&](int t0, const frag* aq, const frag* ao, f32x16& sv, f32x16& dpv) {
 #pragma unroll
         for (int t = 0; t < SB; ++t) {
-          sv = E::mma(aq[t], kf[t0 + t], sv);
-          dpv = E::mma(ao[t], vf[t0 + t], dpv);
+          frag a = aq[t], o = ao[t];
+          to_agpr(a);      // at the consumer: a pin right after the read
+          to_agpr(o);      // would make the read wait for its data there
+          sv = E::mma(a, kf[t0 + t], sv);
+          dpv = E::mma(o, vf[t0 + t], dpv);
         }
       };
       // Dropout keep bits of query half qh: bit r for register r (query
@@ -299,15 +300,16 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
             ot[b] = trans_frag<T, D>(sdO, b, 2 * qh + t, lane);
             qt[b] = trans_frag<T, D>(sQ, b, 2 * qh + t, lane);
           }
-          to_agpr(ot[b]);
-          to_agpr(qt[b]);
         }
       };
       auto dvdk_mma = [&](const frag* ot, const frag* qt, const frag& pf, const frag& df) {
 #pragma unroll
         for (int b = 0; b < ND; ++b) {
-          dvacc[b] = E::mma(ot[b], pf, dvacc[b]);
-          dkacc[b] = E::mma(qt[b], df, dkacc[b]);
+          frag o = ot[b], q = qt[b];
+          to_agpr(o);
+          to_agpr(q);
+          dvacc[b] = E::mma(o, pf, dvacc[b]);
+          dkacc[b] = E::mma(q, df, dkacc[b]);
         }
       };
 

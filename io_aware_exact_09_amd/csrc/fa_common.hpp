@@ -243,7 +243,9 @@ __device__ __forceinline__ void interleave() {
   }
 }
 
-// Pin an MFMA operand fragment to the accumulation registers (AGPRs).
+// Pin an MFMA operand fragment to the accumulation registers (AGPRs).  The
+// empty asm reads the value, so the compiler waits for the load that produced
+// it at this point: call it just before the MFMA that consumes the fragment.
 template <typename F>
 __device__ __forceinline__ void to_agpr(F& f) {
   if constexpr (sizeof(f) == 16) {
