@@ -252,17 +252,33 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
         return mine_of(IntTag<0>{}) | mine_of(IntTag<1>{}) | mine_of(IntTag<2>{}) |
                mine_of(IntTag<3>{});
       };
+      // d = 128: the LSE and D rows a P/dS part needs are read one MFMA
+      // block ahead (read in the same block they queue behind that block's
+      // operand reads, and the arithmetic waits for all of them), and each
+      // part's results are anchored in its block (see pds_part).  At d = 64
+      // the blocks are too short for either and both measured slower.
+      constexpr bool LOOK = D == 128 && NQH == 2;
+      auto stat_load = [&](int qh, int a0, int a1, f32x4* lv, f32x4* dv) {
+#pragma unroll
+        for (int a = a0; a < a1; ++a) {
+          const int qi = 32 * qh + 8 * a + 4 * g;
+          lv[a - a0] = *reinterpret_cast<const f32x4*>(sLt + qi);
+          dv[a - a0] = *reinterpret_cast<const f32x4*>(sDt + qi);
+        }
+      };
       // P = 2^(S c - LSE log2 e), dS = P (dP - D) for register groups
-      // a0 .. a1-1 (register r holds query 32qh + 8(r/4) + 4g + r%4).
-      auto pds_part = [&](int qh, int a0, int a1, f32x16& sv, f32x16& dpv) {
+      // a0 .. a1-1 (register r holds query 32qh + 8(r/4) + 4g + r%4), with the
+      // statistics from stat_load (LOOK) or read here.
+      auto pds_part = [&](int qh, int a0, int a1, f32x16& sv, f32x16& dpv,
+                          const f32x4* lvs = nullptr, const f32x4* dvs = nullptr) {
         if constexpr (DROP) {
           if (a0 == 0) kbits[qh] = drop_bits(qh);
         }
 #pragma unroll
         for (int a = a0; a < a1; ++a) {
           const int qi = 32 * qh + 8 * a + 4 * g;
-          const f32x4 lv = *reinterpret_cast<const f32x4*>(sLt + qi);
-          const f32x4 dv = *reinterpret_cast<const f32x4*>(sDt + qi);
+          const f32x4 lv = LOOK ? lvs[a - a0] : *reinterpret_cast<const f32x4*>(sLt + qi);
+          const f32x4 dv = LOOK ? dvs[a - a0] : *reinterpret_cast<const f32x4*>(sDt + qi);
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
             const int r = 4 * a + x;
@@ -279,6 +295,14 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
               dpv[r] = p * (dpv[r] - dv[x]);
             }
           }
+        }
+        // The arithmetic is pure and its results are next used blocks later,
+        // so instruction selection would place it there, past this block's
+        // scheduling fence (leaving this block's MFMAs without VALU work and
+        // a later block with too much); an empty asm use keeps it here.
+        if constexpr (LOOK) {
+#pragma unroll
+          for (int r = 4 * a0; r < 4 * a1; ++r) asm volatile("" ::"v"(sv[r]), "v"(dpv[r]));
         }
       };
       auto pds_pack = [&](const f32x16& sv, const f32x16& dpv, frag* pf, frag* df) {
@@ -321,6 +345,12 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
         f32x16 s1 = f32x16{}, dp1 = f32x16{};
         frag pf1[2], df1[2];
         frag ta[ND], tb[ND], ua[ND], ub[ND];
+        constexpr int GP = 4 / NSB;             // register groups of P/dS per S/dP block
+        f32x4 lc[GP], dc[GP], ln[GP], dn[GP];   // LOOK: statistics in use / being read
+        auto stat_next = [&]() {
+#pragma unroll
+          for (int t = 0; t < GP; ++t) { lc[t] = ln[t]; dc[t] = dn[t]; }
+        };
         sdp_read(0, 0, xa, xb);
         sched_fence();
         // S/dP, half 0
@@ -328,8 +358,10 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
         for (int k = 0; k < NSB; ++k) {
           if (k + 1 < NSB) sdp_read(0, (k + 1) * SB, ya, yb);
           else sdp_read(1, 0, ya, yb);
+          if (LOOK && k + 1 == NSB) stat_load(0, 0, GP, lc, dc);
           sdp_mma(k * SB, xa, xb, s0, dp0);
-          interleave<2 * SB, 2 * SB, 0>();
+          if (LOOK && k + 1 == NSB) interleave<2 * SB, 2 * SB + 2 * GP, 0>();
+          else interleave<2 * SB, 2 * SB, 0>();
           sched_fence();
 #pragma unroll
           for (int t = 0; t < SB; ++t) { xa[t] = ya[t]; xb[t] = yb[t]; }
@@ -339,26 +371,33 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
         for (int k = 0; k < NSB; ++k) {
           if (k + 1 < NSB) sdp_read(1, (k + 1) * SB, ya, yb);
           else dvdk_read(0, 0, ta, tb);
+          if constexpr (LOOK) {
+            if (k + 1 < NSB) stat_load(0, (k + 1) * GP, (k + 2) * GP, ln, dn);
+            else stat_load(1, 0, 2, ln, dn);
+          }
           sdp_mma(k * SB, xa, xb, s1, dp1);
-          pds_part(0, k * 4 / NSB, (k + 1) * 4 / NSB, s0, dp0);
+          pds_part(0, k * GP, (k + 1) * GP, s0, dp0, lc, dc);
           if (k + 1 == NSB) pds_pack(s0, dp0, pf0, df0);
-          if (k + 1 < NSB) interleave<2 * SB, 2 * SB + 8 / NSB, 5>();
-          else interleave<2 * SB, 4 * ND + 8 / NSB, 5>();
+          if (k + 1 < NSB) interleave<2 * SB, 2 * SB + 2 * GP, 5>();
+          else interleave<2 * SB, 4 * ND + (LOOK ? 4 : 2 * GP), 5>();
           sched_fence();
 #pragma unroll
           for (int t = 0; t < SB; ++t) { xa[t] = ya[t]; xb[t] = yb[t]; }
+          if constexpr (LOOK) stat_next();
         }
         // dV/dK, half 0, with P/dS of half 1 in between
         dvdk_read(0, 1, ua, ub);
+        if constexpr (LOOK) stat_load(1, 2, 4, ln, dn);
         dvdk_mma(ta, tb, pf0[0], df0[0]);
-        pds_part(1, 0, 2, s1, dp1);
+        pds_part(1, 0, 2, s1, dp1, lc, dc);
         interleave<2 * ND, 4 * ND + 4, 6>();
         sched_fence();
+        if constexpr (LOOK) stat_next();
         dvdk_read(1, 0, ta, tb);
         dvdk_mma(ua, ub, pf0[1], df0[1]);
-        pds_part(1, 2, 4, s1, dp1);
+        pds_part(1, 2, 4, s1, dp1, lc, dc);
         pds_pack(s1, dp1, pf1, df1);
-        interleave<2 * ND, 4 * ND + 4, 6>();
+        interleave<2 * ND, 4 * ND + (LOOK ? 0 : 4), 6>();
         sched_fence();
         // dV/dK, half 1
         dvdk_read(1, 1, ua, ub);
