@@ -1,6 +1,7 @@
 """Turn rocprofv3 output into the short text summaries kept under profiles/.
 
-    python -m io_aware_exact_09_amd.profiles stats <kernel_stats.csv> <out.md> "<command>"
+    python -m io_aware_exact_09_amd.profiles stats <kernel_stats.csv> <out.md> "<command>" \
+        [<kernel_trace.csv> <warmup> <steps>]
     python -m io_aware_exact_09_amd.profiles traffic <fetch_dir> <write_dir> <workload> \
         <out.json> "<fetch command>" "<write command>"
     python -m io_aware_exact_09_amd.profiles counters <out.md> <workload> \
@@ -34,6 +35,7 @@ ROOT = os.path.dirname(HERE)
 PROFILES = os.path.join(ROOT, "profiles")
 
 KERNELS = ("fa_fwd_kernel", "fa_fwd_pp_kernel", "fa_bwd_delta_kernel", "fa_bwd_dkdv_kernel",
+           "fa_bwd_dkdv_reduce_kernel",
            "fa_bwd_dq_kernel", "fa_decode_split_kernel", "fa_decode_combine_kernel",
            "fa_fwd_fp8_kernel")
 
@@ -84,14 +86,40 @@ def _rows(path_or_dir: str, suffix: str):
             yield from csv.DictReader(f)
 
 
-def stats_summary(stats_csv: str, command: str) -> str:
-    lines = ["# rocprofv3 kernel-trace summary", "", f"Command: `{command}`", "",
-             "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
-             "|---|---|---|---|---|---|"]
+def stats_summary(stats_csv: str, command: str, trace_csv: str | None = None,
+                  warmup: int = 0, steps: int = 0) -> str:
+    """Per-kernel calls and durations from a --kernel-trace --stats run.
+
+    With the per-dispatch trace and the bench's warm-up / timed step counts
+    (one launch of each kernel per step), a last column averages only the
+    dispatches of the timed steps: the launches the bench's HIP events time.
+    """
+    timed = {}
+    if trace_csv:
+        per = {}
+        rows = sorted(_rows(trace_csv, "kernel_trace.csv"), key=lambda r: int(r["Dispatch_Id"]))
+        for r in rows:
+            per.setdefault(short_name(r["Kernel_Name"]), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        for k, v in per.items():
+            if len(v) >= warmup + steps and steps > 0:
+                timed[k] = statistics.fmean(v[warmup:warmup + steps])
+    lines = ["# rocprofv3 kernel-trace summary", "", f"Command: `{command}`", ""]
+    head = "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |"
+    if timed:
+        lines += [f"Last column: average over dispatches {warmup + 1}..{warmup + steps} of each "
+                  f"kernel, the {steps} timed steps after {warmup} warm-up steps (the bench's "
+                  "HIP-event window; later dispatches are its cold-cache steps).", ""]
+        head += " timed steps average (us) |"
+    lines += [head, "|" + "---|" * (head.count("|") - 1)]
     for r in _rows(stats_csv, "kernel_stats.csv"):
-        lines.append("| {} | {} | {:.1f} | {:.1f} | {:.1f} | {:.1f}% |".format(
-            short_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3,
-            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+        k = short_name(r["Name"])
+        line = "| {} | {} | {:.1f} | {:.1f} | {:.1f} | {:.1f}% |".format(
+            k, r["Calls"], float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"]))
+        if timed:
+            line += f" {timed[k]:.1f} |" if k in timed else " |"
+        lines.append(line)
     return "\n".join(lines) + "\n"
 
 
@@ -206,7 +234,8 @@ def counters_table(passes, workload: str) -> str:
 
 def main(argv):
     if argv[0] == "stats":
-        text = stats_summary(argv[1], argv[3])
+        extra = (argv[4], int(argv[5]), int(argv[6])) if len(argv) > 6 else ()
+        text = stats_summary(argv[1], argv[3], *extra)
         open(argv[2], "w").write(text)
         print(text)
     elif argv[0] == "traffic":
