@@ -27,6 +27,7 @@
 
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
+#include "fa_rows.hpp"
 
 namespace fa {
 
@@ -495,6 +496,27 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
     }
     return;
   }
+  if constexpr (sizeof(T) == 2) {
+    // Results through LDS (fa_rows.hpp, padded rows): dV in lds0, dK in lds1.
+    static_assert(BK * RowTile<T, D, true>::RS <= 2 * STB, "result rows must fit a staging array");
+    __syncthreads();                                  // every wave is done with the tiles
+    const float vs = DROP ? drp.inv_keep : 1.0f;
+    const int lr = 32 * w + l32;
+#pragma unroll
+    for (int b = 0; b < ND; ++b)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int col = 32 * b + 8 * a + 4 * g;
+        put_row4<T, D, true>(lds0, lr, col, dvacc[b][4 * a] * vs, dvacc[b][4 * a + 1] * vs,
+                             dvacc[b][4 * a + 2] * vs, dvacc[b][4 * a + 3] * vs);
+        put_row4<T, D, true>(lds1, lr, col, dkacc[b][4 * a] * scale, dkacc[b][4 * a + 1] * scale,
+                             dkacc[b][4 * a + 2] * scale, dkacc[b][4 * a + 3] * scale);
+      }
+    __syncthreads();
+    write_rows<T, D, true, BK, kThreads>(lds0, dV + head + (size_t)k0 * D, N - k0, tid);
+    write_rows<T, D, true, BK, kThreads>(lds1, dK + head + (size_t)k0 * D, N - k0, tid);
+    return;
+  }
   if (krow < N) {
     T* dKr = dK + head + (size_t)krow * D;
     T* dVr = dV + head + (size_t)krow * D;
@@ -738,6 +760,21 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
     }
   }
 
+  if constexpr (sizeof(T) == 2) {
+    // Results through LDS (fa_rows.hpp; padded rows would not fit).
+    static_assert(BR * D * (int)sizeof(T) <= 2 * TB, "result rows must fit a staging array");
+    __syncthreads();                                  // every wave is done with the tiles
+#pragma unroll
+    for (int b = 0; b < ND; ++b)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        put_row4<T, D, false>(lds0, 32 * w + l32, 32 * b + 8 * a + 4 * g, dqacc[b][4 * a] * scale,
+                              dqacc[b][4 * a + 1] * scale, dqacc[b][4 * a + 2] * scale,
+                              dqacc[b][4 * a + 3] * scale);
+    __syncthreads();
+    write_rows<T, D, false, BR, kThreads>(lds0, dQ + head + (size_t)q0 * D, N - q0, tid);
+    return;
+  }
   if (qrow < N) {
     T* dQr = dQ + head + (size_t)qrow * D;
 #pragma unroll

@@ -28,6 +28,7 @@
 
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
+#include "fa_rows.hpp"
 
 namespace fa {
 
@@ -250,7 +251,23 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   // ---- epilogue ----------------------------------------------------------------
   const float l_tot = sum_xor32(l_run);
   const float inv = l_tot > 0.f ? (DROP ? dp.inv_keep : 1.0f) / l_tot : 0.f;
-  if (qrow < N) {
+  if (qrow < N && g == 0)
+    LSE[(size_t)bh * N + qrow] =
+        l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : neg_inf();
+  if constexpr (sizeof(T) == 2) {
+    // O through LDS (fa_rows.hpp; padded rows would not fit).
+    static_assert(BR * D * (int)sizeof(T) <= 2 * TB, "O rows must fit a staging array");
+    __syncthreads();                                  // every wave is done with the tiles
+#pragma unroll
+    for (int b = 0; b < ND; ++b)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        put_row4<T, D, false>(lds0, 32 * w + l32, 32 * b + 8 * a + 4 * g, oacc[b][4 * a] * inv,
+                              oacc[b][4 * a + 1] * inv, oacc[b][4 * a + 2] * inv,
+                              oacc[b][4 * a + 3] * inv);
+    __syncthreads();
+    write_rows<T, D, false, BR, kThreads>(lds0, O + head + (size_t)q0 * D, N - q0, tid);
+  } else if (qrow < N) {
     T* Orow = O + head + (size_t)qrow * D;
 #pragma unroll
     for (int b = 0; b < ND; ++b)
@@ -258,9 +275,6 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
       for (int a = 0; a < 4; ++a)
         E::store4(Orow + 32 * b + 8 * a + 4 * g, oacc[b][4 * a] * inv, oacc[b][4 * a + 1] * inv,
                   oacc[b][4 * a + 2] * inv, oacc[b][4 * a + 3] * inv);
-    if (g == 0)
-      LSE[(size_t)bh * N + qrow] =
-          l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : neg_inf();
   }
 }
 
@@ -492,18 +506,24 @@ fa_fwd_pp_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
 
   const float l_tot = sum_xor32(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (qrow < N) {
-    T* Orow = O + head + (size_t)qrow * D;
+  if (qrow < N && g == 0)
+    LSE[(size_t)bh * N + qrow] =
+        l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : neg_inf();
+  // O through LDS (fa_rows.hpp, unpadded): group G's 128 rows in slot G.
+  static_assert(128 * D * (int)sizeof(T) <= 2 * TB, "O rows must fit a ring slot");
+  __syncthreads();                                    // every wave is done with the ring
+  unsigned char* so = G == 0 ? slot0 : slot1;
 #pragma unroll
-    for (int b = 0; b < ND; ++b)
+  for (int b = 0; b < ND; ++b)
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-        E::store4(Orow + 32 * b + 8 * a + 4 * g, oacc[b][4 * a] * inv, oacc[b][4 * a + 1] * inv,
-                  oacc[b][4 * a + 2] * inv, oacc[b][4 * a + 3] * inv);
-    if (g == 0)
-      LSE[(size_t)bh * N + qrow] =
-          l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : neg_inf();
-  }
+    for (int a = 0; a < 4; ++a)
+      put_row4<T, D, false>(so, 32 * wg + l32, 32 * b + 8 * a + 4 * g, oacc[b][4 * a] * inv,
+                            oacc[b][4 * a + 1] * inv, oacc[b][4 * a + 2] * inv,
+                            oacc[b][4 * a + 3] * inv);
+  __syncthreads();
+  const int g0 = q0 + 128 * G;
+  write_rows<T, D, false, 128, kThreads>(so, O + head + (size_t)g0 * D, N - g0,
+                                         tid & (kThreads - 1));
 }
 
 template <typename T, int D, bool CAUSAL>

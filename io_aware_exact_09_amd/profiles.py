@@ -42,7 +42,7 @@ KERNELS = ("fa_fwd_kernel", "fa_fwd_pp_kernel", "fa_bwd_delta_kernel", "fa_bwd_d
 # Device sources of each kernel family (host-side files such as fa_api.cpp
 # do not change what a kernel does on the GPU).
 SOURCES = {
-    "train": ("fa_common.hpp", "fa_launch.hpp", "fa_fwd.hip", "fa_bwd.hip"),
+    "train": ("fa_common.hpp", "fa_launch.hpp", "fa_rows.hpp", "fa_fwd.hip", "fa_bwd.hip"),
     "decode": ("fa_common.hpp", "fa_decode.hpp", "fa_decode.hip"),
     "fp8": ("fa_common.hpp", "fa_launch.hpp", "fa_fwd_fp8.hip"),
 }
