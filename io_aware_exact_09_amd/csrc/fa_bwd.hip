@@ -646,7 +646,6 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   // the register budget, so other tiles carry no mask arithmetic).
   auto tile = [&](auto mask_sel, auto buf_sel, int kv0) {
     const bool MASKED_TILE = mask_sel;
-    const int BUF = buf_sel;
     const unsigned char* sK = pick(buf_sel, lds0, lds1);
     const unsigned char* sV = sK + TB;
 #pragma unroll
@@ -726,7 +725,6 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
     }
   };
   auto step = [&](auto buf_sel, int j, int jn) {
-    const int BUF = buf_sel;
     wait_global_loads();
     __syncthreads();
     const int kv0 = j * BC;
@@ -740,7 +738,43 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
       tile(need_mask, buf_sel, kv0);
     }
   };
-  if constexpr (sizeof(T) == 2) {
+  if constexpr (sizeof(T) == 2 && !CAUSAL && !DROP) {
+    // Without the causal mask only the sequence's last tile can need the
+    // masked body.  With both bodies in one loop the register allocator
+    // kept both live and spilled at d = 128, so the walk runs as two loops,
+    // unmasked tiles then the rest, each with one body; two tiles per trip,
+    // buffer index compile-time (`odd`: the next tile is in buffer 1).
+    // (The causal walk below, with the same two bodies chosen per tile,
+    // compiles free of spills; the dropout bodies do not fit either way.)
+    auto step_as = [&](auto buf_sel, auto mask_sel, int j, int jn) {
+      wait_global_loads();
+      __syncthreads();
+      if (jn < ntiles) stage(jn, other(buf_sel));
+      tile(mask_sel, buf_sel, j * BC);
+    };
+    bool odd = false;
+    auto walk = [&](auto mask_sel) {
+      constexpr bool MT = decltype(mask_sel)::value;
+      auto more = [&](int jj) { return jj < ntiles && (MT || jj * BC + BC <= N); };
+      if (odd && more(j)) {
+        const int jn = next_kept(j + 1);
+        step_as(IntTag<1>{}, mask_sel, j, jn);
+        j = jn;
+        odd = false;
+      }
+      while (more(j)) {
+        int jn = next_kept(j + 1);
+        step_as(IntTag<0>{}, mask_sel, j, jn);
+        j = jn;
+        if (!more(j)) { odd = true; break; }
+        jn = next_kept(j + 1);
+        step_as(IntTag<1>{}, mask_sel, j, jn);
+        j = jn;
+      }
+    };
+    walk(BoolTag<false>{});
+    walk(BoolTag<true>{});
+  } else if constexpr (sizeof(T) == 2) {
     while (j < ntiles) {   // two tiles per trip, buffer index compile-time
       int jn = next_kept(j + 1);
       step(IntTag<0>{}, j, jn);

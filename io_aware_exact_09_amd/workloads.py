@@ -91,6 +91,9 @@ WORKLOADS = {
     # drawn as for long (x20 rows included), then quantized by quantize_fp8
     "long_fp8": Workload("long_fp8", 2, 16, 4096, 128, "fp8", True,
                          k_row_frac=0.01, k_row_gain=20.0, seed=1007),
+    # the long-context shape without the causal mask (every query row sees
+    # every key, as in an encoder), iid N(0, 1) inputs
+    "long_nc": Workload("long_nc", 2, 16, 4096, 128, "bf16", False, seed=1008),
 }
 
 

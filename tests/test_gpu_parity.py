@@ -232,7 +232,7 @@ def test_workload_tiny_full_oracle():
         assert np.abs(got[n] - ref[n]).max() <= 1e-4, n
 
 
-@pytest.mark.parametrize("name", ["gpt2", "long", "sparse", "verylong"])
+@pytest.mark.parametrize("name", ["gpt2", "long", "sparse", "verylong", "long_nc"])
 def test_workload_full_size_sampled(name):
     w = W.WORKLOADS[name]
     x = W.make_inputs(w)
