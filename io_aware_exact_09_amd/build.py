@@ -11,6 +11,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -54,6 +55,32 @@ def _compile(src: str, extra: list[str]) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
+
+
+_REMARK = re.compile(r"remark: +(Function Name|TotalSGPRs|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|"
+                     r"Occupancy \[waves/SIMD\]|SGPRs Spill|VGPRs Spill|"
+                     r"LDS Size \[bytes/block\]): (\S+)")
+
+
+def resource_usage(src: str) -> dict[str, dict[str, int]]:
+    """Per-kernel register, scratch, occupancy and LDS figures of one source
+    file, from a device-only compile with the compiler's resource-usage
+    remarks: {mangled kernel name: {"VGPRs": .., "AGPRs": .., "ScratchSize":
+    .., "Occupancy": .., "VGPRs Spill": .., "SGPRs Spill": .., "LDS Size": ..}}."""
+    cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", os.devnull, "--cuda-device-only",
+           "-Rpass-analysis=kernel-resource-usage"] + common_flags()
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stderr}")
+    out: dict[str, dict[str, int]] = {}
+    cur = None
+    for m in _REMARK.finditer(r.stderr):
+        key, val = m.group(1), m.group(2)
+        if key == "Function Name":
+            cur = out.setdefault(val, {})
+        elif cur is not None:
+            cur[key.split(" [")[0]] = int(val)
+    return out
 
 
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
