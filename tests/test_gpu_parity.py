@@ -176,6 +176,41 @@ def test_extreme_logits_stay_finite():
         assert lse_err.max() <= 1e-4, (dtype, lse_err.max())
 
 
+@pytest.mark.parametrize("dtype,d,causal", [("fp32", 64, False), ("bf16", 128, True),
+                                            ("bf16", 128, False)])
+def test_shift_invariances(dtype, d, causal):
+    """K -> K + c moves every logit of row i by scale*q_i.c (over whichever
+    keys the row keeps), so O, dQ, dK and dV stay put and LSE moves by that
+    amount; V -> V + c moves O by c and leaves dQ, dK, dV unchanged (the row
+    sums of dS vanish).  K, V and c sit on a grid of multiples of 1/8 so the
+    shifted inputs are exact in bf16: any difference comes from the kernels.
+    Each pair is compared against the other run within the dtype's bar."""
+    N = 300
+    inp = W.random_inputs(1, 2, N, d, dtype, seed=61 + d)
+    rng = np.random.default_rng(17)
+    grid = lambda *shape: (rng.integers(-16, 17, size=shape) / 8.0).astype(np.float32)
+    inp["k"], inp["v"] = grid(1, 2, N, d), grid(1, 2, N, d)
+    c = (rng.integers(-8, 9, size=d) / 8.0).astype(np.float32)
+    scale = 1 / math.sqrt(d)
+    base = run_hip(inp, dtype, scale, causal)
+
+    shk = run_hip(dict(inp, k=inp["k"] + c), dtype, scale, causal)
+    lse_shift = scale * np.einsum("bhnd,d->bhn", inp["q"].astype(np.float64), c.astype(np.float64))
+    tol_check("LSE", shk["LSE"], base["LSE"] + lse_shift, dtype)
+    for n in ("O", "dQ", "dK", "dV"):
+        e = tol_check(n, shk[n], base[n], dtype)
+        _say(f"  K+c {dtype} d={d} causal={causal} {n}: " +
+             " ".join(f"{kk}={vv:.3e}" for kk, vv in e.items()))
+
+    shv = run_hip(dict(inp, v=inp["v"] + c), dtype, scale, causal)
+    tol_check("O", shv["O"], base["O"] + c.astype(np.float64), dtype)
+    tol_check("LSE", shv["LSE"], base["LSE"], dtype)
+    for n in ("dQ", "dK", "dV"):
+        e = tol_check(n, shv[n], base[n], dtype)
+        _say(f"  V+c {dtype} d={d} causal={causal} {n}: " +
+             " ".join(f"{kk}={vv:.3e}" for kk, vv in e.items()))
+
+
 def test_determinism_bitwise():
     """No atomics: two runs give bit-identical outputs."""
     w = W.WORKLOADS["gpt2"].with_shape(B=2, H=4)
