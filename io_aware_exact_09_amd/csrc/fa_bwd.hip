@@ -730,11 +730,13 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
     const int kv0 = j * BC;
     if (jn < ntiles) stage(jn, other(buf_sel));
     const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > q0 + 32 * w);
-    if constexpr (sizeof(T) == 2) {
+    if constexpr (sizeof(T) == 2 && !(DROP && !CAUSAL && D == 128)) {
       // Separate masked / unmasked bodies where the registers allow it.
       if (need_mask) tile(BoolTag<true>{}, buf_sel, kv0);
       else tile(BoolTag<false>{}, buf_sel, kv0);
     } else {
+      // One body with the mask under a wave-uniform branch: the fp32 path
+      // and the non-causal dropout path at d = 128 have no registers for two.
       tile(need_mask, buf_sel, kv0);
     }
   };

@@ -24,9 +24,11 @@ SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_fwd_fp8.hip"]
 # float as "f32", integers and bools as Python values.
 #
 # Known to spill: the dQ pass with dropout, bf16, d = 128, without the causal
-# mask (block mask on or off).  The Philox state and keep bits do not fit the
-# 256 registers of two waves per SIMD next to the tile's operands in either
-# loop structure; the causal and d = 64 dropout kernels do fit.
+# mask (block mask on or off).  Next to the tile's operands, the Philox state
+# and keep bits leave no room in the 256 registers of two waves per SIMD for
+# a second tile body; with one body (the mask under a wave-uniform branch)
+# 5-13 VGPRs still spill, against ~105 with two.  The causal and d = 64
+# dropout kernels fit.
 SCRATCH_ALLOWED = {
     ("fa_bwd_dq_kernel", ("bf16", 128, False, False, True)),
     ("fa_bwd_dq_kernel", ("bf16", 128, False, True, True)),
