@@ -20,7 +20,10 @@ step; peak is the published MI355X dense bf16 MFMA rate, 2.5 PFLOP/s (fp32
 MFMA 157.3 TFLOP/s for fp32 workloads).
 
 The cpu_baseline leg times the CPU fp64 oracle on a bounded sample of the same
-workload (whole heads, about 10-30 s) on this host's cores.
+workload (whole heads, about 10-30 s) on this host's cores.  Secondary fields:
+cold_cache (steps after a 512 MiB write that evicts the caches) and
+two_stream_step (the dK/dV and dQ passes on two streams through the phase
+entry points; the headline step is fa_bwd's single stream).
 
 Decode workloads (--workload decode | decode_mix | decode_spec): a step is one
 fa_decode call over the whole batch (64 sequences, 8K cache, 32 query heads
