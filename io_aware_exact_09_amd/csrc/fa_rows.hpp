@@ -10,9 +10,12 @@
 //
 // Tile layout: with PAD, rows are D*e + 16 bytes apart (row r starts 4 banks
 // after row r-1); without it, rows are unpadded and the 16-byte chunks of
-// row r are XOR-swizzled by r mod (chunks per row).  Both keep the 8-byte
-// writes of a half-wave (16 rows x 2 lanes) on distinct banks; PAD needs
-// 16 more bytes per row of LDS.
+// row r are XOR-swizzled by the row's index among the rows that start on
+// the same bank: r itself when a row spans all 64 banks (256 bytes), r / 2
+// when it spans half of them (128 bytes, so rows alternate between the two
+// halves).  Both keep the 8-byte writes of a half-wave (16 rows x 2 lanes)
+// and the row reads of 16 lanes on distinct banks; PAD needs 16 more bytes
+// per row of LDS.
 #pragma once
 
 #include "fa_common.hpp"
@@ -24,7 +27,10 @@ struct RowTile {
   static constexpr int RBo = D * (int)sizeof(T);          // bytes of one output row
   static constexpr int CPR = RBo / 16;                    // 16-byte chunks per row
   static constexpr int RS = RBo + (PAD ? 16 : 0);         // row stride in the tile
-  __device__ static int chunk(int row, int c) { return PAD ? c : c ^ (row & (CPR - 1)); }
+  static constexpr int RPS = RBo >= 256 ? 1 : 256 / RBo;  // rows per 256-byte bank span
+  __device__ static int chunk(int row, int c) {
+    return PAD ? c : c ^ ((row / RPS) & (CPR - 1));
+  }
 };
 
 // Four values of row `row`, columns col .. col+3 (col a multiple of 4).
