@@ -33,8 +33,15 @@
  *  - causal != 0 keeps key j for query i only when j <= i (self-attention,
  *    N queries against N keys).
  *  - d must be 64 or 128; N >= 1 (any N: the last tile is masked by bounds);
- *    B, H >= 1; N * d and B * H * ceil(N/128) must fit in int32.
- *  - scale must be finite and >= 0 (1/sqrt(d) is the usual value).
+ *    B, H >= 1; N * d and B * H * ceil(N/128) must fit in int32, and one
+ *    head's rows, N rounded up to a multiple of 256, times d times the element
+ *    size must not exceed 2^32 - 1 bytes (the kernels address a head with
+ *    32-bit byte offsets): N <= 8388352 for fp32 at d = 128, N <= 16776960
+ *    for bf16 at d = 128.  Larger sizes give FA_ERR_SHAPE.
+ *  - scale may be any finite value: [Training-FA] §1 writes
+ *    softmax(Q K^T / sqrt(d)) V and [FA-guide] "Problem ve motivasyon" the
+ *    unscaled Q K^T, so the scale is a free parameter (1/sqrt(d) is the usual
+ *    value; a negative scale flips the sign of every score).
  *  - Outputs must not overlap inputs or each other.
  *  - Validation runs before anything is enqueued; on any error nothing is
  *    written and no kernel is launched.  A launch failure is reported as
@@ -55,18 +62,30 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = 1,       /* a required pointer is NULL */
-  FA_ERR_SHAPE = 2,      /* B, H or N < 1, or a size overflows int32 */
+  FA_ERR_SHAPE = 2,      /* B, H or N < 1, a size overflows int32, or one head
+                            spans 2^32 bytes or more */
   FA_ERR_HEAD_DIM = 3,   /* d not in {64, 128} */
   FA_ERR_DTYPE = 4,      /* dtype not an fa_dtype value */
   FA_ERR_ALIGN = 5,      /* a tensor pointer is misaligned */
   FA_ERR_WORKSPACE = 6,  /* workspace NULL, misaligned or too small */
   FA_ERR_LAUNCH = 7,     /* the HIP runtime refused a kernel launch */
-  FA_ERR_ARG = 8,        /* scale not finite or negative, dropout_p outside [0, 1),
-                            or num_splits outside [0, 1024] */
-  FA_ERR_ALIAS = 9       /* an output overlaps an input or another output */
+  FA_ERR_ARG = 8,        /* scale not finite, dropout_p outside [0, 1), or
+                            num_splits outside [0, 1024] */
+  FA_ERR_ALIAS = 9,      /* an output overlaps an input or another output */
+  /* Not statuses: these two give the enum the whole range of int, so that any
+     int a caller passes or compares is a valid value of the type. */
+  FA_STATUS_INT_MIN_ = -2147483647 - 1,
+  FA_STATUS_INT_MAX_ = 2147483647
 } fa_status;
 
-typedef enum { FA_BF16 = 0, FA_FP32 = 1 } fa_dtype;
+typedef enum {
+  FA_BF16 = 0,
+  FA_FP32 = 1,
+  /* Not element types: the whole range of int is a valid value of the type,
+     so any int a caller passes reaches the check (FA_ERR_DTYPE). */
+  FA_DTYPE_INT_MIN_ = -2147483647 - 1,
+  FA_DTYPE_INT_MAX_ = 2147483647
+} fa_dtype;
 
 #define FA_MASK_BLOCK 128
 
@@ -96,7 +115,8 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
  * fa_bwd_workspace_bytes -- size of the scratch buffer fa_bwd needs: one fp32
  * per query row (D_i = sum_k dO_ik O_ik), i.e. 4 * B * H * N bytes, so the
  * backward's extra memory is O(N) ([FA-guide] "Karmaşıklık Analizi").
- * Returns 0 for sizes that fa_bwd would reject with FA_ERR_SHAPE.
+ * The size does not depend on the element type.  Returns 0 for sizes that
+ * fa_bwd rejects with FA_ERR_SHAPE for either element type.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 
@@ -271,8 +291,9 @@ fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* Vt8, const floa
  *                 16-byte aligned, caller-owned, contents overwritten.
  *
  * Hq must be a multiple of Hkv (FA_ERR_SHAPE otherwise); B, Hq, Hkv, Nq,
- * Nkv >= 1; Nkv * d and B * Hq * Nq * d must fit in int32; seqlens 4-byte
- * aligned.  Other conventions as above.
+ * Nkv >= 1; Nkv * d and B * Hq * Nq * d must fit in int32, and one cache
+ * head (Nkv rows) and one group's Hq / Hkv * Nq query rows obey the 2^32-byte
+ * head bound above; seqlens 4-byte aligned.  Other conventions as above.
  */
 fa_status fa_decode(const void* Q, const void* K, const void* V, const int* seqlens, void* O,
                     float* LSE, int B, int Hq, int Hkv, int Nq, int Nkv, int d, float scale,

@@ -37,6 +37,15 @@ struct Shape {
   uintptr_t mask_bytes() const { const uintptr_t t = (N + 127) / 128; return t * t; }
 };
 
+// The kernels address the rows of one head through 32-bit byte offsets into
+// a buffer descriptor (rows up to the next multiple of 256 past N are formed,
+// and read as zeros), so one head's rows, rounded up to 256, must span fewer
+// than 2^32 bytes.
+bool head_fits_u32(long long rows, int d, unsigned elem) {
+  const unsigned long long padded = ((unsigned long long)rows + 255) / 256 * 256;
+  return padded * (unsigned long long)d * elem <= 0xFFFFFFFFull;
+}
+
 fa_status check_shape(const Shape& s, float scale) {
   if (s.dtype != FA_BF16 && s.dtype != FA_FP32) return FA_ERR_DTYPE;
   if (s.B < 1 || s.H < 1 || s.N < 1) return FA_ERR_SHAPE;
@@ -44,9 +53,9 @@ fa_status check_shape(const Shape& s, float scale) {
   const long long bh = (long long)s.B * s.H;
   const long long tiles = (s.N + 127LL) / 128;
   if (bh > INT_MAX || (long long)s.N * s.d > INT_MAX || bh * tiles > INT_MAX ||
-      bh * s.N > INT_MAX)
+      bh * s.N > INT_MAX || !head_fits_u32(s.N, s.d, s.dtype == FA_BF16 ? 2 : 4))
     return FA_ERR_SHAPE;
-  if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_ARG;
   return FA_OK;
 }
 
@@ -413,7 +422,7 @@ namespace {
 struct DecShape {
   int B, Hq, Hkv, Nq, Nkv, d;
   fa_dtype dtype;
-  int R() const { return (Hq / Hkv) * Nq; }
+  long long R() const { return (long long)(Hq / Hkv) * Nq; }   // call once Hq % Hkv == 0
   uintptr_t elem() const { return dtype == FA_BF16 ? 2 : 4; }
   uintptr_t q_bytes() const { return (uintptr_t)B * Hq * Nq * d * elem(); }
   uintptr_t kv_bytes() const { return (uintptr_t)B * Hkv * Nkv * d * elem(); }
@@ -425,10 +434,15 @@ fa_status check_decode_shape(const DecShape& s, int num_splits) {
   if (s.B < 1 || s.Hq < 1 || s.Hkv < 1 || s.Nq < 1 || s.Nkv < 1) return FA_ERR_SHAPE;
   if (s.Hq % s.Hkv) return FA_ERR_SHAPE;
   if (s.d != 64 && s.d != 128) return FA_ERR_HEAD_DIM;
-  const long long qe = (long long)s.B * s.Hq * s.Nq * s.d;
-  const long long pairs = (long long)s.B * s.Hkv;
-  const long long groups = pairs * ((s.R() + 31) / 32) * ((s.Nkv + 127) / 128);
-  if ((long long)s.Nkv * s.d > INT_MAX || qe > INT_MAX || groups > INT_MAX)
+  // Each product is formed only once its factors are known to be small
+  // enough not to overflow 64 bits.
+  const long long bq = (long long)s.B * s.Hq;
+  if (bq > INT_MAX || bq * s.Nq > INT_MAX || bq * s.Nq * s.d > INT_MAX) return FA_ERR_SHAPE;
+  const long long pairs = (long long)s.B * s.Hkv;            // <= B * Hq
+  const long long qgroups = pairs * ((s.R() + 31) / 32);     // R <= Hq * Nq
+  if (qgroups > INT_MAX || qgroups * ((s.Nkv + 127LL) / 128) > INT_MAX ||
+      (long long)s.Nkv * s.d > INT_MAX || !head_fits_u32(s.Nkv, s.d, (unsigned)s.elem()) ||
+      !head_fits_u32(s.R(), s.d, (unsigned)s.elem()))
     return FA_ERR_SHAPE;
   if (num_splits < 0 || num_splits > 1024) return FA_ERR_ARG;
   return FA_OK;
@@ -444,14 +458,14 @@ FA_EXPORT int fa_decode_num_splits(int B, int Hq, int Hkv, int Nq, int Nkv, int 
                                    int num_splits) {
   const DecShape s{B, Hq, Hkv, Nq, Nkv, d, FA_BF16};
   if (check_decode_shape(s, num_splits) != FA_OK) return 0;
-  return fa::decode_plan(B, Hkv, s.R(), Nkv, num_splits).S;
+  return fa::decode_plan(B, Hkv, (int)s.R(), Nkv, num_splits).S;
 }
 
 FA_EXPORT size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nkv, int d,
                                            int num_splits) {
   const DecShape s{B, Hq, Hkv, Nq, Nkv, d, FA_BF16};
   if (check_decode_shape(s, num_splits) != FA_OK) return 0;
-  return decode_workspace(s, fa::decode_plan(B, Hkv, s.R(), Nkv, num_splits));
+  return decode_workspace(s, fa::decode_plan(B, Hkv, (int)s.R(), Nkv, num_splits));
 }
 
 FA_EXPORT fa_status fa_decode(const void* Q, const void* K, const void* V, const int* seqlens,
@@ -461,8 +475,8 @@ FA_EXPORT fa_status fa_decode(const void* Q, const void* K, const void* V, const
   FA_TRY(check_buffers({{Q, 0, 0}, {K, 0, 0}, {V, 0, 0}}, {{O, 0, 0}, {LSE, 0, 0}}));
   const DecShape s{B, Hq, Hkv, Nq, Nkv, d, dtype};
   FA_TRY(check_decode_shape(s, num_splits));
-  if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_ARG;
-  const fa::DecodePlan plan = fa::decode_plan(B, Hkv, s.R(), Nkv, num_splits);
+  if (!std::isfinite(scale)) return FA_ERR_ARG;
+  const fa::DecodePlan plan = fa::decode_plan(B, Hkv, (int)s.R(), Nkv, num_splits);
   const size_t need = decode_workspace(s, plan);
   const Buf q{Q, s.q_bytes(), 16}, k{K, s.kv_bytes(), 16}, v{V, s.kv_bytes(), 16};
   const Buf o{O, s.q_bytes(), 16}, l{LSE, s.rows() * 4, 4};
@@ -477,7 +491,7 @@ FA_EXPORT fa_status fa_decode(const void* Q, const void* K, const void* V, const
   a.opart = need ? static_cast<float*>(workspace) : nullptr;
   a.lpart = need ? static_cast<float*>(workspace) + s.rows() * plan.S * d : nullptr;
   a.pairs = B * Hkv;
-  a.Hkv = Hkv; a.Nq = Nq; a.R = s.R(); a.Nkv = Nkv; a.d = d;
+  a.Hkv = Hkv; a.Nq = Nq; a.R = (int)s.R(); a.Nkv = Nkv; a.d = d;
   a.S = plan.S; a.chunk = plan.chunk;
   a.scale = scale;
   a.causal = causal != 0;
@@ -491,15 +505,15 @@ FA_EXPORT const char* fa_status_str(fa_status s) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "null pointer argument";
     case FA_ERR_SHAPE:
-      return "invalid shape (sizes must be >= 1 and fit int32; Hq a multiple of Hkv)";
+      return "invalid shape (sizes must be >= 1 and fit int32, one head's rows must span "
+             "under 4 GiB; Hq a multiple of Hkv)";
     case FA_ERR_HEAD_DIM: return "head dimension must be 64 or 128";
     case FA_ERR_DTYPE: return "unknown dtype";
     case FA_ERR_ALIGN: return "misaligned tensor pointer (16 bytes; LSE 4 bytes)";
     case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_ARG:
-      return "scale must be finite and >= 0; dropout probability in [0, 1); num_splits in "
-             "[0, 1024]";
+      return "scale must be finite; dropout probability in [0, 1); num_splits in [0, 1024]";
     case FA_ERR_ALIAS: return "an output overlaps an input or another output";
   }
   return "unknown status";

@@ -8,7 +8,10 @@
 // through softmax (the closed form that the page's garbled dQ/dK stand for):
 //
 //   D_i = sum_k dO_ik O_ik
-//   P_ij = 2^(S_ij * c - LSE_i * log2 e)      (c = scale * log2 e)
+//   P_ij = 2^(S_ij * c - LSE_i * log2 e)      (c = scale * log2 e, of either
+//                                              sign: the backward masks P by
+//                                              a select after the exponential,
+//                                              so it needs no c > 0)
 //   dV_j = sum_i P_ij dO_i,   dP_ij = <dO_i, V_j>,   dS_ij = P_ij (dP_ij - D_i)
 //   dK_j = scale * sum_i dS_ij Q_i,   dQ_i = scale * sum_j dS_ij K_j
 //

@@ -40,13 +40,27 @@ constexpr int kThreads = 256;   // 4 waves per work-group
 // this many doublings (see fa_fwd.hip); probabilities stay <= 2^kLazy.
 constexpr float kLazy = 8.0f;
 
-// Exponent coefficient c = scale * log2(e), clamped to at least FLT_MIN so
-// that c > 0: a masked score (-inf) then always gives 2^(-inf * c) = 0.  For
-// scale = 0 every kept exponent is 2^(s * FLT_MIN - m) with |s * FLT_MIN| far
-// below half an ulp of 1, i.e. exactly the values scale = 0 gives.
+// Exponent coefficient handed to the kernels: |c| = |scale| * log2(e),
+// clamped to at least FLT_MIN, carrying the sign of scale.  The forward
+// kernels set masked scores to -inf before the row max, so they split it with
+// split_coef and work with the positive |c| (then 2^(-inf * |c|) = 0 and |c|
+// times the row max of the kept scores is the row max of S * |c|); for
+// scale < 0 they flip the sign of Q in registers, which is exact, so they form
+// -S and -S * |c| = scale * log2(e) * S.  The backward kernels mask P with a
+// select after the exponential and use the signed c as it is; their final dQ
+// and dK multiplications use the signed scale.  For scale = 0 every kept
+// exponent is 2^(s * FLT_MIN - m) with |s * FLT_MIN| far below half an ulp of
+// 1, i.e. exactly the values scale = 0 gives.
 inline float score_coef(float scale) {
-  const float c = scale * kLog2e;
-  return c < 1.17549435e-38f ? 1.17549435e-38f : c;
+  float c = (scale < 0.f ? -scale : scale) * kLog2e;
+  c = c < 1.17549435e-38f ? 1.17549435e-38f : c;
+  return scale < 0.f ? -c : c;
+}
+
+// Kernel side of score_coef: returns |c| and whether the scores must be negated.
+__device__ __forceinline__ float split_coef(float c, bool& negate_scores) {
+  negate_scores = c < 0.f;
+  return negate_scores ? -c : c;
 }
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
@@ -243,6 +257,15 @@ __device__ __forceinline__ void interleave() {
   }
 }
 
+// Flip the sign of every value of an operand fragment (a sign-bit XOR: exact,
+// and -x of a finite value is always representable).
+__device__ __forceinline__ void negate(Elem<__bf16>::frag& f) {
+  f.v = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, f.v) ^ 0x80008000u);
+}
+__device__ __forceinline__ void negate(Elem<float>::frag& f) {
+  f.lo = -f.lo;
+  f.hi = -f.hi;
+}
 // Pin an MFMA operand fragment to the accumulation registers (AGPRs).  The
 // empty asm reads the value, so the compiler waits for the load that produced
 // it at this point: call it just before the MFMA that consumes the fragment.

@@ -70,7 +70,7 @@ fa_decode_split_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                        const T* __restrict__ V, const int32_t* __restrict__ seqlens,
                        T* __restrict__ O, float* __restrict__ LSE, float* __restrict__ Opart,
                        float* __restrict__ Lpart, int Hkv, int Nq, int R, int RG, int Nkv,
-                       int S, int chunk, int P, float c /* scale*log2e, > 0 */) {
+                       int S, int chunk, int P, float c /* score_coef(scale) */) {
   using E = Elem<T>;
   using frag = typename E::frag;
   using Cfg = DecCfg<T, D, WAVES, NBUF>;
@@ -123,6 +123,12 @@ fa_decode_split_kernel(const T* __restrict__ Q, const T* __restrict__ K,
 #pragma unroll
   for (int t = 0; t < NT; ++t)
     qf[t] = gload_frag<T>(rq, (uint32_t)r * RB + (16 * t + 8 * g) * sizeof(T));
+  bool negs;
+  c = split_coef(c, negs);   // c = |scale| log2(e); Q negated when scale < 0
+  if (negs) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) negate(qf[t]);
+  }
 
   auto stage = [&](int i, auto slot) {
     const int kv0 = kb + i * KT;
@@ -281,8 +287,8 @@ fa_decode_split_kernel(const T* __restrict__ Q, const T* __restrict__ K,
         acc += e * *reinterpret_cast<const f32x4*>(so + ((x * 32 + j) * NC + (ch ^ (j & (NC - 1)))) * 4);
       }
     }
-    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-    const float lse = lsum > 0.f ? (M + __builtin_amdgcn_logf(lsum)) * kLn2 : neg_inf();
+    const float inv = lsum != 0.f ? 1.0f / lsum : 0.f;
+    const float lse = lsum != 0.f ? (M + __builtin_amdgcn_logf(lsum)) * kLn2 : neg_inf();
     const size_t row = row0 + j;
     if (S == 1) {
       E::store4(O + row * D + 4 * ch, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
@@ -319,11 +325,11 @@ fa_decode_combine_kernel(const float* __restrict__ Opart, const float* __restric
       for (int k = 0; k < PER; ++k) acc[k] = fmaf(e, op[(size_t)x * D + 64 * k], acc[k]);
     }
   }
-  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  const float inv = den != 0.f ? 1.0f / den : 0.f;
   T* orow = O + (size_t)row * D + lane;
 #pragma unroll
   for (int k = 0; k < PER; ++k) orow[64 * k] = (T)(acc[k] * inv);
-  if (lane == 0) LSE[row] = den > 0.f ? M + __builtin_amdgcn_logf(den) * kLn2 : neg_inf();
+  if (lane == 0) LSE[row] = den != 0.f ? M + __builtin_amdgcn_logf(den) * kLn2 : neg_inf();
 }
 
 template <typename T, int D, bool CAUSAL>

@@ -17,7 +17,8 @@
 // Softmax Takibi") in its deferred-normalisation form (snula.amonoc.com/
 // course/ru/week-13.html, Step 2: keep (m, d, o) per query block, scale the
 // old d and o by e^(m_old - m_new) on a new maximum).  Scores live in the
-// log2 domain: c = scale * log2(e), so every exponential is one v_exp_f32.
+// log2 domain: c = |scale| * log2(e), so every exponential is one v_exp_f32
+// (a negative scale flips the sign of Q in registers instead; score_coef).
 // A row whose running max is still -inf uses 0 as the subtrahend, so no
 // 2^(-inf - (-inf)) is formed (week-13 page, "Типичные ошибки").
 //
@@ -43,7 +44,7 @@ __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(Occupancy<T, D>::fwd, Occupancy<T, D>::fwd)))
 fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
               T* __restrict__ O, float* __restrict__ LSE, const uint8_t* __restrict__ mask,
-              int BH, int kv_group, int N, int T_tiles, float c /* scale*log2e, > 0 */,
+              int BH, int kv_group, int N, int T_tiles, float c /* score_coef(scale) */,
               DropParams dp) {
   using E = Elem<T>;
   using frag = typename E::frag;
@@ -77,6 +78,12 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
 #pragma unroll
   for (int t = 0; t < NT; ++t)
     qf[t] = gload_frag<T>(rq, (uint32_t)qrow * RB + (16 * t + 8 * g) * sizeof(T));
+  bool negs;
+  c = split_coef(c, negs);   // from here on c = |scale| log2(e) > 0
+  if (negs) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) negate(qf[t]);
+  }
 
   const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
   const int ntiles = (kv_end + BC - 1) / BC;
@@ -250,10 +257,10 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
 
   // ---- epilogue ----------------------------------------------------------------
   const float l_tot = sum_xor32(l_run);
-  const float inv = l_tot > 0.f ? (DROP ? dp.inv_keep : 1.0f) / l_tot : 0.f;
+  const float inv = l_tot != 0.f ? (DROP ? dp.inv_keep : 1.0f) / l_tot : 0.f;
   if (qrow < N && g == 0)
     LSE[(size_t)bh * N + qrow] =
-        l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : neg_inf();
+        l_tot != 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : neg_inf();
   if constexpr (sizeof(T) == 2) {
     // O through LDS (fa_rows.hpp; padded rows would not fit).
     static_assert(BR * D * (int)sizeof(T) <= 2 * TB, "O rows must fit a staging array");
@@ -326,7 +333,7 @@ __global__ void __launch_bounds__(2 * kThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd_pp_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                  T* __restrict__ O, float* __restrict__ LSE, int BH, int kv_group, int N,
-                 float c /* scale*log2e, > 0 */) {
+                 float c /* score_coef(scale) */) {
   static_assert(sizeof(T) == 2, "bf16 only");
   using E = Elem<T>;
   using frag = typename E::frag;
@@ -357,6 +364,12 @@ fa_fwd_pp_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
 #pragma unroll
   for (int t = 0; t < NT; ++t)
     qf[t] = gload_frag<T>(rq, (uint32_t)qrow * RB + (16 * t + 8 * g) * sizeof(T));
+  bool negs;
+  c = split_coef(c, negs);   // from here on c = |scale| log2(e) > 0
+  if (negs) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) negate(qf[t]);
+  }
 
   // Tiles of the work-group, and of this wave's group (causal: the first
   // group's rows end 128 keys earlier).
@@ -505,10 +518,10 @@ fa_fwd_pp_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   }
 
   const float l_tot = sum_xor32(l_run);
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  const float inv = l_tot != 0.f ? 1.0f / l_tot : 0.f;
   if (qrow < N && g == 0)
     LSE[(size_t)bh * N + qrow] =
-        l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : neg_inf();
+        l_tot != 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : neg_inf();
   // O through LDS (fa_rows.hpp, unpadded): group G's 128 rows in slot G.
   static_assert(128 * D * (int)sizeof(T) <= 2 * TB, "O rows must fit a ring slot");
   __syncthreads();                                    // every wave is done with the ring

@@ -83,7 +83,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
                   const float* __restrict__ sK, const float* __restrict__ sV,
                   __bf16* __restrict__ O, float* __restrict__ LSE,
                   const uint8_t* __restrict__ mask, int BH, int N, int T_tiles,
-                  float c /* scale*log2e, > 0 */) {
+                  float c /* score_coef(scale) */) {
   constexpr int BR = 128, BC = 64;
   constexpr int NT = D / 64;               // 64-wide d chunks (S^T MFMAs per 32 keys)
   constexpr int ND = D / 32;               // 32-wide d blocks of O^T
@@ -113,6 +113,12 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
     const u32x4 a = buf_load16(rq, off), b = buf_load16(rq, off + 16);
     qf[t] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3],
                   (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+  }
+  bool negs;
+  c = split_coef(c, negs);   // c = |scale| log2(e); Q negated when scale < 0
+  if (negs) {              // E4M3: bit 7 of each code is its sign
+#pragma unroll
+    for (int t = 0; t < NT; ++t) qf[t] ^= (int)0x80808080u;
   }
   const int T = (N + kMaskBlock - 1) / kMaskBlock;
   const float cq = c * sQ[(size_t)bh * T + q0 / kMaskBlock];
@@ -268,7 +274,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
 
   // ---- epilogue ------------------------------------------------------------------
   const float l_tot = sum_xor32(l_run);
-  const float inv = l_tot > 0.f ? sV[bh] / l_tot : 0.f;
+  const float inv = l_tot != 0.f ? sV[bh] / l_tot : 0.f;
   if (qrow < N) {
     __bf16* Orow = O + head + (size_t)qrow * D;
 #pragma unroll
@@ -280,7 +286,7 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
                              oacc[b][4 * a + 3] * inv);
     if (g == 0)
       LSE[(size_t)bh * N + qrow] =
-          l_tot > 0.f ? (m_run - kShift + __builtin_amdgcn_logf(l_tot)) * kLn2 : neg_inf();
+          l_tot != 0.f ? (m_run - kShift + __builtin_amdgcn_logf(l_tot)) * kLn2 : neg_inf();
   }
 }
 

@@ -142,6 +142,18 @@ def _check_tensors(ref: torch.Tensor, named: dict):
             raise ValueError(f"{name} must be contiguous")
 
 
+def _scratch(nbytes: int, ref: torch.Tensor, stream=None) -> torch.Tensor:
+    """Device scratch of ``nbytes`` bytes for one call, allocated by torch's
+    caching allocator on the current stream.  When the call is enqueued on
+    another ``stream``, the block is also recorded as in use by that stream,
+    so the allocator does not hand it to a later allocation until the
+    kernels reading and writing it there have finished."""
+    ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=ref.device)
+    if stream is not None:
+        ws.record_stream(stream)
+    return ws
+
+
 def fa_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
     return int(load_library().fa_bwd_workspace_bytes(B, H, N, d))
 
@@ -172,9 +184,8 @@ def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = False,
     lib = load_library()
     _check_tensors(q, dict(q=q, k=k, v=v, o=o, do=do, lse=lse, dq=dq, dk=dk, dv=dv))
     B, H, N, d = q.shape
-    need = fa_bwd_workspace_bytes(B, H, N, d)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = _scratch(fa_bwd_workspace_bytes(B, H, N, d), q, stream)
     wbytes = workspace.numel() * workspace.element_size()
     if block_mask is not None:
         _check_tensors(q, dict(block_mask=block_mask))
@@ -209,8 +220,7 @@ def fa_bwd_dropout(q, k, v, o, do, lse, dq, dk, dv, scale: float, dropout_p: flo
     _mask_ok(q, block_mask)
     B, H, N, d = q.shape
     if workspace is None:
-        workspace = torch.empty(max(fa_bwd_workspace_bytes(B, H, N, d), 1), dtype=torch.uint8,
-                                device=q.device)
+        workspace = _scratch(fa_bwd_workspace_bytes(B, H, N, d), q, stream)
     st = lib.fa_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
                             _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
                             _ptr(block_mask), float(dropout_p), int(seed) & (2 ** 64 - 1),
@@ -292,7 +302,7 @@ def fa_bwd_gqa(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = Fal
     B, Hq, N, d = q.shape
     if workspace is None:
         need = int(lib.fa_bwd_gqa_workspace_bytes(B, Hq, k.shape[1], N, d))
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = _scratch(need, q, stream)
     st = lib.fa_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
                         _ptr(dk), _ptr(dv), B, Hq, k.shape[1], N, d, float(scale),
                         int(bool(causal)), _ptr(block_mask), _dtype_code(q), _ptr(workspace),
@@ -345,7 +355,7 @@ def fa_decode(q, k, v, o, lse, scale: float, seqlens=None, causal: bool = False,
             raise TypeError("seqlens must be int32")
     need = fa_decode_workspace_bytes(B, Hq, Hkv, Nq, Nkv, d, num_splits)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _scratch(need, q, stream)
     wbytes = 0 if workspace is None else _nbytes(workspace)
     st = lib.fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(seqlens), _ptr(o), _ptr(lse), B, Hq, Hkv,
                        Nq, Nkv, d, float(scale), int(bool(causal)), int(num_splits),
@@ -354,19 +364,28 @@ def fa_decode(q, k, v, o, lse, scale: float, seqlens=None, causal: bool = False,
 
 
 # Convenience wrappers that allocate outputs with torch (memory plumbing only).
+# The outputs come from torch's current stream; when the work is enqueued on
+# another ``stream`` they are recorded as in use there too (see _scratch).
+
+def _mark(stream, *ts):
+    if stream is not None:
+        for t in ts:
+            t.record_stream(stream)
+
 
 def decode(q, k, v, scale: float, seqlens=None, causal: bool = False, num_splits: int = 0,
            workspace=None, stream=None):
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    _mark(stream, o, lse)
     fa_decode(q, k, v, o, lse, scale, seqlens, causal, num_splits, workspace, stream)
     return o, lse
-
 
 
 def forward(q, k, v, scale: float, causal: bool = False, block_mask=None, stream=None):
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    _mark(stream, o, lse)
     fa_fwd(q, k, v, o, lse, scale, causal, block_mask, stream)
     return o, lse
 
@@ -374,5 +393,6 @@ def forward(q, k, v, scale: float, causal: bool = False, block_mask=None, stream
 def backward(q, k, v, o, do, lse, scale: float, causal: bool = False, block_mask=None,
              workspace=None, stream=None):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _mark(stream, dq, dk, dv)
     fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale, causal, block_mask, workspace, stream)
     return dq, dk, dv

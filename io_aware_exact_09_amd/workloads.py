@@ -15,8 +15,8 @@ The five workloads stand in for the shapes the FlashAttention reading guide
   sparse    B=4  H=8  N=8192  d=64   bf16  128-tile block mask, Bernoulli(0.25)
                                            keep pattern plus the diagonal
   verylong  B=1  H=8  N=16384 d=128  bf16  causal         sigma = 0.5
-  long_gqa  as long (without the x20 rows), 4 key/value heads shared by
-            the 16 query heads
+  long_gqa  as long (1% of K rows x20), 4 key/value heads shared by the
+            16 query heads
   long_fp8  as long, quantized to FP8 (E4M3) for the FP8 forward
 
 Recipe (the same for every workload): ``rng = numpy.random.default_rng(seed)``
@@ -85,8 +85,9 @@ WORKLOADS = {
                          sigma=0.5, seed=1005),
     # long-context training with grouped key/value heads (4 query heads per
     # key/value head, the grouping of the week-13 page's Llama-3-8B example),
-    # iid N(0, 1) inputs
-    "long_gqa": Workload("long_gqa", 2, 16, 4096, 128, "bf16", True, seed=1006, Hkv=4),
+    # with the long workload's large logits: 1% of the K rows x20
+    "long_gqa": Workload("long_gqa", 2, 16, 4096, 128, "bf16", True,
+                         k_row_frac=0.01, k_row_gain=20.0, seed=1006, Hkv=4),
     # the long-context shape as FP8 (E4M3) inputs for the FP8 forward: Q, K, V
     # drawn as for long (x20 rows included), then quantized by quantize_fp8
     "long_fp8": Workload("long_fp8", 2, 16, 4096, 128, "fp8", True,

@@ -146,9 +146,12 @@ def o_error_bound(q8, k8, vt8, sq, sk, sv, scale: float, causal: bool = False,
 
 
 def head_rows(q8, k8, vt8, sq, sk, sv, b: int, h: int, rows, scale: float,
-              causal: bool = False, block_mask=None, mask_block: int = MASK_BLOCK):
-    """O, LSE and the P-rounding bound of ``o_error_bound`` for the query rows
-    ``rows`` of head (b, h) (full-size checks on a sample)."""
+              causal: bool = False, block_mask=None, mask_block: int = MASK_BLOCK,
+              shift: int = 8):
+    """O, LSE and the P-rounding bound of ``o_error_bound`` (same ``shift``)
+    for the query rows ``rows`` of head (b, h) (full-size checks on a
+    sample): the same formulas as ``forward`` and ``o_error_bound``,
+    restricted to those rows."""
     from .attention import keep_rows
     sl = (slice(b, b + 1), slice(h, h + 1))
     q, k, v = dequantize(q8[sl], k8[sl], vt8[sl], np.asarray(sq)[sl], np.asarray(sk)[sl],
@@ -158,5 +161,5 @@ def head_rows(q8, k8, vt8, sq, sk, sv, b: int, h: int, rows, scale: float,
     keep = keep_rows(rows, k.shape[0], causal, block_mask, mask_block)
     p, o, lse = _head_forward(q[rows], k, v, scale, keep)
     av = np.abs(decode(vt8[b, h]).T)
-    bound = float(sv[b, h]) * (2.0 ** -4 * (p @ av) + 2.0 ** -18 * (keep @ av))
+    bound = float(sv[b, h]) * (2.0 ** -4 * (p @ av) + 2.0 ** (-10 - shift) * (keep @ av))
     return {"O": o, "LSE": lse, "bound": bound}

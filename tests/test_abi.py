@@ -78,7 +78,7 @@ def bwd(lib, q=p(0), k=p(1), v=p(2), o=p(3), do=p(4), lse=p(5), dq=p(6), dk=p(7)
     (dict(d=96), 3), (dict(d=32), 3), (dict(d=256), 3),
     (dict(dtype=7), 4),
     (dict(q=p(0, 8)), 5), (dict(o=p(3, 4)), 5), (dict(lse=p(4, 2)), 5),
-    (dict(scale=float("nan")), 8), (dict(scale=float("inf")), 8), (dict(scale=-0.5), 8),
+    (dict(scale=float("nan")), 8), (dict(scale=float("inf")), 8), (dict(scale=-float("inf")), 8),
     (dict(o=p(0, 64)), 9), (dict(lse=p(2, 16)), 9), (dict(o=p(4)), 9),
     (dict(mask=p(3, 32)), 9),
 ])
@@ -91,7 +91,7 @@ def test_fwd_validation(lib, kw, code):
     (dict(N=0), 2), (dict(d=80), 3), (dict(dtype=-1), 4),
     (dict(dk=p(7, 8)), 5), (dict(lse=p(5, 1)), 5),
     (dict(ws=None), 6), (dict(wsb=4 * 2 * 128 - 1), 6), (dict(ws=p(9, 4)), 6),
-    (dict(scale=-1.0), 8),
+    (dict(scale=float("-inf")), 8),
     (dict(dq=p(0, 16)), 9), (dict(dk=p(6, 16)), 9), (dict(ws=p(5)), 9), (dict(dv=p(9)), 9),
     (dict(mask=p(8, 16)), 9),
 ])
@@ -154,7 +154,7 @@ def test_gqa_validation(lib):
     # fwd: (Q, K, V, O, LSE, B, Hq, Hkv, N, d, scale, causal, mask, dtype, stream)
     f = [p(0), p(1), p(2), p(3), p(4), 2, 8, 2, 128, 64, 0.125, 1, None, BF16, None]
     for idx, val, code in ((6, 7, 2), (7, 3, 2), (7, 0, 2), (7, 16, 2), (0, None, 1),
-                           (9, 80, 3), (13, 9, 4), (10, -1.0, 8), (3, p(1, 64), 9)):
+                           (9, 80, 3), (13, 9, 4), (10, float("nan"), 8), (3, p(1, 64), 9)):
         bad = list(f); bad[idx] = val
         assert lib.fa_fwd_gqa(*bad) == code, (idx, val)
     # K spans B * Hkv heads: an output starting inside its last head overlaps it
@@ -247,7 +247,7 @@ def test_phase_validation(lib):
     assert lib.fa_bwd_dkdv(*bad) == 6
     bad = list(args); bad[6] = p(7)            # dV over the workspace (read by the pass)
     assert lib.fa_bwd_dkdv(*bad) == 9
-    bad = list(args); bad[11] = -1.0
+    bad = list(args); bad[11] = float("inf")
     assert lib.fa_bwd_dkdv(*bad) == 8
     # dq: (Q, K, V, dO, LSE, dQ, B, H, N, d, scale, causal, mask, dtype, ws, wsb, stream)
     args = [p(0), p(1), p(2), p(3), p(4), p(5), 1, 2, 128, 64, 0.125, 1, None, BF16, p(7),
@@ -265,3 +265,46 @@ def test_single_hip_runtime_in_process(lib):
     maps = open("/proc/self/maps").read()
     paths = {ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln}
     assert len(paths) == 1, paths
+
+
+@pytest.mark.parametrize("scale", [-0.125, -1.0, -0.0, -1e30, 3.4e38])
+def test_any_finite_scale_passes_validation(lib, scale):
+    """Any finite scale, negative included, passes the argument checks: each
+    call below is stopped by the next check in order (a misaligned pointer)."""
+    assert fwd(lib, scale=scale, q=p(0, 8)) == 5
+    assert bwd(lib, scale=scale, dk=p(7, 8)) == 5
+    assert fwd_drop(lib, scale=scale, q=p(0, 8)) == 5
+    f = [p(0, 8), p(1), p(2), p(3), p(4), 2, 8, 2, 128, 64, scale, 1, None, BF16, None]
+    assert lib.fa_fwd_gqa(*f) == 5
+    f8 = [p(0), p(1), p(2, 4), p(3), p(4), p(5), p(6), p(7), 2, 4, 256, 128, scale, 1, None,
+          None]
+    assert lib.fa_fwd_fp8(*f8) == 5
+    assert dec(lib, scale=scale, q=p(0, 8)) == 5
+
+
+# One head's rows, rounded up to 256, times d times the element size must not
+# exceed 2^32 - 1 bytes: the largest accepted N for d = 128 is 2^23 - 256 in
+# fp32 and 2^24 - 256 in bf16.
+@pytest.mark.parametrize("N,dtype,ok", [
+    ((1 << 23) - 256, FP32, True), ((1 << 23) - 255, FP32, False), (1 << 23, FP32, False),
+    ((1 << 24) - 256, BF16, True), ((1 << 24) - 255, BF16, False),
+])
+def test_head_bytes_fit_32_bit_offsets(lib, N, dtype, ok):
+    # accepted shapes are stopped by the next check (a misaligned pointer)
+    want = 5 if ok else 2
+    assert fwd(lib, N=N, d=128, dtype=dtype, B=1, H=1, q=p(0, 8)) == want
+    assert bwd(lib, N=N, d=128, dtype=dtype, B=1, H=1, dk=p(7, 8)) == want
+    assert lib.fa_bwd_preprocess(p(0), p(1, 8), 1, 1, N, 128, dtype, p(2), 1 << 30,
+                                 None) == want
+    f8_ok = ok if dtype == BF16 else True        # FP8 codes: the bf16 bound (O is bf16)
+    if N % 16 == 0:
+        f8 = [p(0), p(1), p(2, 4), p(3), p(4), p(5), p(6), p(7), 1, 1, N, 128, 0.1, 1, None,
+              None]
+        assert lib.fa_fwd_fp8(*f8) == (5 if f8_ok else 2)
+
+
+@pytest.mark.parametrize("Nkv,dtype,ok", [
+    ((1 << 23) - 256, FP32, True), (1 << 23, FP32, False), ((1 << 24) - 256, BF16, True),
+])
+def test_decode_cache_head_fits_32_bit_offsets(lib, Nkv, dtype, ok):
+    assert dec(lib, Nkv=Nkv, dtype=dtype, ns=1, q=p(0, 8)) == (5 if ok else 2)

@@ -123,3 +123,15 @@ def test_small_against_dropout_oracle(N, d, dtype, causal, mk, p):
     for n in OUTS:
         e = tol_check(n, got[n], ref[n], dtype)
         _say(f"  {n}: " + " ".join(f"{k}={v:.3e}" for k, v in e.items()))
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp32", 64)])
+def test_negative_scale(dtype, d):
+    """Any finite scale: dropout with a negative one against the oracle."""
+    inp = W.random_inputs(1, 2, 300, d, dtype, seed=57)
+    got = run_dropout(inp, dtype, -0.1, True, None, 0.2, 1234)
+    ref = od.forward_backward(inp["q"], inp["k"], inp["v"], inp["do"], -0.1, _f32(0.2), 1234,
+                              True, None)
+    for n in OUTS:
+        e = tol_check(n, got[n], ref[n], dtype)
+        _say(f"  {n}: " + " ".join(f"{k}={v:.3e}" for k, v in e.items()))

@@ -1,0 +1,155 @@
+"""GPU parity at full size: every head of the benchmark's workloads against the
+CPU fp64 oracle, in the launch configuration the benchmark times (fa_fwd then
+fa_bwd on one stream, the same seeded inputs).
+
+The pages claim the tiled result is exact up to summation order (the
+week-13 course page, Step 2), so the whole output tensors are compared:
+
+* relative Frobenius error <= 1e-2 on O, dQ, dK, dV (whole tensors; the worst
+  single head is printed too);
+* max-abs error <= 2e-2 literally on the workloads whose outputs stay within
+  a few units (gpt2, sparse, verylong, long_nc: there the bf16 rounding of
+  the exact answer is far below 2e-2, so a literal miss would be a kernel
+  error); on long and long_gqa, where dQ reaches ~90 and the rounding of the
+  exact answer alone is ~0.24, the bar is 2e-2 * max(1, max|ref|);
+* LSE within 1e-4 * max(1, |LSE|).
+
+Next to every max-abs error the bf16 rounding floor max|bf16(ref) - ref| is
+printed.  The verylong workload (8 heads of 16384 rows; the full oracle needs
+~8 GiB per head) is compared on 512 query rows and 512 key rows of every head
+through the oracle's row helpers.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import gqa
+from oracle import fp8 as OF
+from io_aware_exact_09_amd import fa
+from io_aware_exact_09_amd import workloads as W
+from gpu_util import device, tol_check, upload, upload_mask
+from test_gpu_fp8 import _check as fp8_check
+
+pytestmark = pytest.mark.gpu
+
+OUTS = ("O", "LSE", "dQ", "dK", "dV")
+LITERAL = {"gpt2", "sparse", "verylong", "long_nc"}
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _floor(ref):
+    """max |bf16(ref) - ref|: the error of the exact answer rounded to bf16."""
+    r32 = ref.astype(np.float32)
+    return float(np.abs(W.bf16_round(r32).astype(np.float64) - ref).max())
+
+
+def _run_workload(w, x):
+    q, k, v, do = (upload(x[n], w.dtype) for n in ("q", "k", "v", "do"))
+    m = upload_mask(x["mask"])
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if w.kv_heads != w.H:
+        fa.fa_fwd_gqa(q, k, v, o, lse, w.scale, w.causal, m)
+        fa.fa_bwd_gqa(q, k, v, o, do, lse, dq, dk, dv, w.scale, w.causal, m)
+    else:
+        fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal, m)
+        fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, w.scale, w.causal, m)
+    torch.cuda.synchronize()
+    return {"O": o, "LSE": lse, "dQ": dq, "dK": dk, "dV": dv}
+
+
+def _compare(name, got, ref, w, label, literal):
+    """Whole-array comparison at the workload's bar; prints the errors, the
+    bf16 floor and the worst head's relative Frobenius error."""
+    e = tol_check(name, got, ref, w.dtype)
+    if name == "LSE":
+        _say(f"  {label} LSE: max-abs {e['max_abs']:.3e}")
+        return
+    fl = _floor(ref)
+    heads = got.reshape(-1, *got.shape[-2:]), ref.reshape(-1, *ref.shape[-2:])
+    per_head = [float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+                for a, b in zip(*heads)]
+    _say(f"  {label} {name}: rel-Fro {e['rel_fro']:.3e} (worst head {max(per_head):.3e}), "
+         f"max-abs {e['max_abs']:.3e} (bf16 floor {fl:.3e}, max|ref| {e['ref_max']:.2f})")
+    if literal:
+        assert e["max_abs"] <= 2e-2, f"{name}: max-abs {e['max_abs']:.3e} > 2e-2 (literal)"
+
+
+@pytest.mark.parametrize("name", ["gpt2", "long", "sparse", "long_nc", "long_gqa"])
+def test_workload_whole_tensors(name):
+    w = W.WORKLOADS[name]
+    x = W.make_inputs(w)
+    _say(f"workload {name}: B={w.B} H={w.H} Hkv={w.kv_heads} N={w.N} d={w.d} "
+         f"causal={w.causal} mask={'yes' if x['mask'] is not None else 'no'}")
+    got = _run_workload(w, x)
+    got = {n: t.float().cpu().numpy().astype(np.float64) for n, t in got.items()}
+    if w.kv_heads != w.H:
+        ref = gqa.forward_backward(x["q"], x["k"], x["v"], x["do"], w.scale, w.causal,
+                                   x["mask"])
+    else:
+        ref = oracle.forward_backward(x["q"], x["k"], x["v"], x["do"], w.scale, w.causal,
+                                      x["mask"])
+    for n in OUTS:
+        _compare(n, got[n], ref[n], w, name, name in LITERAL)
+
+
+def test_verylong_rows_of_every_head():
+    """B=1, H=8, N=16384, d=128, causal, sigma 0.5: 512 query rows (O, LSE,
+    dQ) and 512 key rows (dK, dV) of every head, always including the first
+    and last rows and both sides of tile boundaries."""
+    w = W.WORKLOADS["verylong"]
+    x = W.make_inputs(w)
+    _say(f"workload verylong: B={w.B} H={w.H} N={w.N} d={w.d}")
+    got = _run_workload(w, x)
+    rng = np.random.default_rng(23)
+    fixed = np.array([0, 1, 63, 64, 127, 128, 255, 256, w.N // 2, w.N - 129, w.N - 128,
+                      w.N - 1])
+    acc = {n: ([], []) for n in OUTS}
+    for h in range(w.H):
+        rows = np.unique(np.concatenate([fixed, rng.choice(w.N, size=512, replace=False)]))
+        qr = oracle.query_rows(x["q"][0, h], x["k"][0, h], x["v"][0, h], x["do"][0, h],
+                               w.scale, rows, w.causal)
+        kr = oracle.key_rows(x["q"][0, h], x["k"][0, h], x["v"][0, h], x["do"][0, h],
+                             w.scale, rows, w.causal)
+        ref = {**qr, **kr}
+        idx = torch.from_numpy(rows).to(device())
+        for n in OUTS:
+            g = got[n][0, h][idx].float().cpu().numpy().astype(np.float64)
+            acc[n][0].append(g)
+            acc[n][1].append(ref[n])
+        _say(f"  head {h}: {len(rows)} rows")
+    for n in OUTS:
+        g, r = np.stack(acc[n][0]), np.stack(acc[n][1])
+        _compare(n, g, r, w, "verylong (sampled rows)", True)
+
+
+def test_long_fp8_whole_output():
+    """The long-context shape quantized to FP8 (the FP8 forward the
+    benchmark times): every head against exact attention on the dequantized
+    inputs, within the probability-rounding bound of the oracle."""
+    w = W.WORKLOADS["long_fp8"]
+    x = W.make_inputs(w)
+    qz = W.quantize_fp8(x["q"], x["k"], x["v"])
+    _say(f"workload long_fp8: B={w.B} H={w.H} N={w.N} d={w.d}")
+    t = {n: torch.from_numpy(np.ascontiguousarray(qz[n])).to(device())
+         for n in ("q8", "k8", "vt8", "sq", "sk", "sv")}
+    o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device=device())
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=device())
+    fa.fa_fwd_fp8(t["q8"], t["k8"], t["vt8"], t["sq"], t["sk"], t["sv"], o, lse, w.scale,
+                  w.causal)
+    torch.cuda.synchronize()
+    args = (qz["q8"], qz["k8"], qz["vt8"], qz["sq"], qz["sk"], qz["sv"], w.scale, w.causal)
+    o_ref, lse_ref = OF.forward(*args)
+    bound = OF.o_error_bound(*args)
+    fp8_check(o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+              o_ref, lse_ref, bound, "long_fp8, all 32 heads")

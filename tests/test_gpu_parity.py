@@ -2,8 +2,9 @@
 the same seeded inputs, element by element.
 
 Small cases run the full oracle and span several tiles plus a ragged tail;
-the five workloads run at full size and are compared on sampled rows, plus
-gradient identities that hold at any size.
+edge cases (dead rows, scale 0, negative scales, large and extreme logits,
+NaN inputs, N = 65536) follow.  The workloads at full size are compared in
+test_gpu_fullsize.py.
 """
 
 from __future__ import annotations
@@ -115,63 +116,94 @@ def test_large_logits(dtype):
 
 
 def _dq_floor_from_bf16_o(inp, scale, causal):
-    """dQ error (rel-Frobenius) that storing O in bf16 alone causes: the
-    backward's D = rowsum(dO * O) is formed from the stored O.  Test-side
-    estimate: exact P and dP, D from the bf16-rounded exact O."""
+    """dQ error (rel-Frobenius) that storing O in bf16 alone causes.
+
+    The backward's row term D_i = sum_k dO_ik O_ik is formed from the O the
+    forward stored (the ABI's O, in bf16).  Test-side estimate from the
+    oracle: exact P, D from the bf16-rounded exact O, and the dQ change that
+    the D difference makes, scale * P (D_exact - D_rounded) K."""
     q, k, v, do = (np.asarray(inp[n], np.float64) for n in ("q", "k", "v", "do"))
     ref = oracle.forward_backward(q, k, v, do, scale, causal)
     N = q.shape[2]
-    keep = np.tril(np.ones((N, N), bool)) if causal else np.ones((N, N), bool)
+    keep = oracle.keep_matrix(N, N, causal)
     err = np.zeros_like(q)
-    for h in range(q.shape[1]):
-        s = np.where(keep, scale * q[0, h] @ k[0, h].T, -np.inf)
-        p = np.exp(s - ref["LSE"][0, h][:, None])
-        d_round = (do[0, h] * W.bf16_round(ref["O"][0, h].astype(np.float32))).sum(1)
-        d_exact = (do[0, h] * ref["O"][0, h]).sum(1)
-        err[0, h] = scale * (p * (d_exact - d_round)[:, None]) @ k[0, h]
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            s_ = np.where(keep, scale * q[b, h] @ k[b, h].T, -np.inf)
+            p = np.exp(s_ - ref["LSE"][b, h][:, None])
+            d_round = (do[b, h] * W.bf16_round(ref["O"][b, h].astype(np.float32))).sum(1)
+            d_exact = (do[b, h] * ref["O"][b, h]).sum(1)
+            err[b, h] = scale * (p * (d_exact - d_round)[:, None]) @ k[b, h]
     return float(np.linalg.norm(err) / np.linalg.norm(ref["dQ"])), ref
+
+
+def _dq_bar(floor):
+    """Bar on the bf16 dQ rel-Frobenius error given the bf16-O storage floor.
+
+    D is formed from the stored bf16 O, as the ABI fixes, so no backward that
+    receives O in bf16 can beat the floor.  The kernel's own roundings (the
+    bf16 P and dS operands) come on top, independently of it; with an exact D
+    they give ~2e-3 on these inputs, so they are allowed 3e-3 and the two
+    add in quadrature (5% slack).  That is the literal 1e-2 whenever the
+    floor is below ~0.9e-2, and only above it a bar that follows the floor."""
+    return max(1e-2, 1.05 * math.hypot(floor, 3e-3))
 
 
 def test_large_logits_dq_tracks_bf16_storage_floor():
     """Few x20 keys per head (3 and 2 of 512): the rows that attend to them
     have dS terms that nearly cancel, and any backward that forms
     D = rowsum(dO * O) from a bf16 O inherits O's rounding there; on this
-    input that floor alone is ~1e-2 rel-Frobenius in dQ.  The kernel's dQ
-    error must stay within 25% of the floor; every other output meets the
-    bar."""
+    input that floor alone is ~0.97e-2 rel-Frobenius in dQ.  Printed: the
+    kernel's dQ error, the floor and the bar applied (_dq_bar); every other
+    output meets the full bar.  A second input with 1% of the keys x20 (the
+    long workload's recipe; floor ~0.78e-2) must meet the literal 1e-2."""
     N, d = 512, 128
+    scale = 1 / math.sqrt(d)
     inp = W.random_inputs(1, 2, N, d, "fp32", seed=13)
     inp["k"][0, 0, [3, 77, 300]] *= 20.0
     inp["k"][0, 1, [5, 400]] *= 20.0
-    inp = {n: W.bf16_round(t) for n, t in inp.items()}
-    scale = 1 / math.sqrt(d)
-    floor, ref = _dq_floor_from_bf16_o(inp, scale, True)
-    got = run_hip(inp, "bf16", scale, True)
-    rel = float(np.linalg.norm(got["dQ"] - ref["dQ"]) / np.linalg.norm(ref["dQ"]))
-    _say(f"  dQ rel-Frobenius {rel:.3e}, floor from bf16 O alone {floor:.3e}")
-    assert rel <= 1.25 * floor + 1e-3
-    for n in ("O", "LSE", "dK", "dV"):
-        tol_check(n, got[n], ref[n], "bf16")
+    cases = [("3+2 keys x20", {n: W.bf16_round(t) for n, t in inp.items()}),
+             ("1% of keys x20", _large_logit_inputs("bf16")[0])]
+    for label, x in cases:
+        floor, ref = _dq_floor_from_bf16_o(x, scale, True)
+        got = run_hip(x, "bf16", scale, True)
+        rel = float(np.linalg.norm(got["dQ"] - ref["dQ"]) / np.linalg.norm(ref["dQ"]))
+        bar = _dq_bar(floor)
+        _say(f"  {label}: dQ rel-Frobenius {rel:.3e}, floor from bf16 O alone {floor:.3e}, "
+             f"bar {bar:.3e}{' (literal)' if bar == 1e-2 else ''}")
+        assert rel <= bar
+        if label.startswith("1%"):
+            assert bar == 1e-2
+        for n in ("O", "LSE", "dK", "dV"):
+            tol_check(n, got[n], ref[n], "bf16")
 
 
 def test_extreme_logits_stay_finite():
     """One K row x1000 (logits in the thousands): every output finite and
-    close to the oracle (fp32 scores of that size carry ~1e-3 absolute
-    rounding, which moves P by ~1e-3 relative)."""
+    close to the oracle.  fp32 scores of that size carry ~1e-3 absolute
+    rounding, which moves P by ~1e-3 relative; bf16 outputs meet the full
+    bar on O, dK, dV and the storage-floor bar on dQ (printed)."""
     N, d = 512, 128
+    scale = 1 / math.sqrt(d)
     for dtype in ("fp32", "bf16"):
         inp = W.random_inputs(1, 2, N, d, "fp32", seed=17)
         inp["k"][0, 1, 11] *= 1000.0
         if dtype == "bf16":        # both sides get the same bf16 values
             inp = {n: W.bf16_round(t) for n, t in inp.items()}
-        got = run_hip(inp, dtype, 1 / math.sqrt(d), True)
-        ref = oracle.forward_backward(inp["q"], inp["k"], inp["v"], inp["do"], 1 / math.sqrt(d),
-                                      True)
+        got = run_hip(inp, dtype, scale, True)
+        floor, ref = _dq_floor_from_bf16_o(inp, scale, True)
         for n in OUTS:
             assert np.isfinite(got[n]).all(), (dtype, n)
         for n in ("O", "dK", "dV"):
             rel = np.linalg.norm(got[n] - ref[n]) / np.linalg.norm(ref[n])
             assert rel <= 1e-2, (dtype, n, rel)
+            if dtype == "bf16":
+                tol_check(n, got[n], ref[n], "bf16")
+        rel = float(np.linalg.norm(got["dQ"] - ref["dQ"]) / np.linalg.norm(ref["dQ"]))
+        bar = _dq_bar(floor) if dtype == "bf16" else 1e-2
+        _say(f"  x1000 {dtype}: dQ rel-Frobenius {rel:.3e} (bar {bar:.3e}, bf16-O floor "
+             f"{floor:.3e})")
+        assert rel <= bar, (dtype, rel, bar)
         lse_err = np.abs(got["LSE"] - ref["LSE"]) / np.maximum(1, np.abs(ref["LSE"]))
         assert lse_err.max() <= 1e-4, (dtype, lse_err.max())
 
@@ -298,40 +330,101 @@ def test_workload_tiny_full_oracle():
         assert np.abs(got[n] - ref[n]).max() <= 1e-4, n
 
 
-@pytest.mark.parametrize("name", ["gpt2", "long", "sparse", "verylong", "long_nc"])
-def test_workload_full_size_sampled(name):
-    w = W.WORKLOADS[name]
-    x = W.make_inputs(w)
-    _say(f"workload {name}: B={w.B} H={w.H} N={w.N} d={w.d}")
-    q, k, v, do = _dev_inputs(x, w.dtype)
-    m = upload_mask(x["mask"])
-    o, lse = fa.forward(q, k, v, w.scale, w.causal, m)
-    dq, dk, dv = fa.backward(q, k, v, o, do, lse, w.scale, w.causal, m)
-    torch.cuda.synchronize()
-    got = {"O": o, "LSE": lse, "dQ": dq, "dK": dk, "dV": dv}
+# --------------------------------------------------------------------------
+# Negative scale: any finite scale is accepted ([Training-FA] §1 scales by
+# 1/sqrt(d), [FA-guide] "Problem ve motivasyon" leaves Q K^T unscaled, so the
+# scale is a free parameter).
+# --------------------------------------------------------------------------
 
-    # Identities over every head (any size): sum_j dK_j = 0, sum_j dV_j = sum_i dO_i.
-    dk_sum = dk.float().sum(dim=2)
-    dk_scale = dk.float().abs().sum(dim=2) + 1e-6
-    assert float((dk_sum.abs() / dk_scale).max()) < 2e-2
-    dv_sum = dv.double().sum(dim=2)
-    do_sum = do.double().sum(dim=2)
-    rel = float((dv_sum - do_sum).norm() / do_sum.norm())
-    _say(f"  identities: max|sum dK|/sum|dK| = {float((dk_sum.abs()/dk_scale).max()):.2e}, "
-         f"|sum dV - sum dO|/|sum dO| = {rel:.2e}")
-    assert rel < 1e-2
+NEG = [
+    # (N, d, dtype, causal, mask-kind): bf16 d = 128 without a mask is the
+    # ping-pong forward; the others the four-wave one
+    (300, 128, "bf16", True, None), (257, 128, "bf16", False, None),
+    (300, 64, "bf16", True, "rand"), (384, 128, "bf16", False, "rand"),
+    (200, 64, "fp32", True, None), (129, 128, "fp32", False, "rand"),
+]
 
-    rng = np.random.default_rng(7)
-    heads = [(0, 0), (w.B - 1, w.H - 1)]
-    for b, h in heads:
-        rows = _sample_rows(w.N, rng)
-        qr = oracle.query_rows(x["q"][b, h], x["k"][b, h], x["v"][b, h], x["do"][b, h],
-                               w.scale, rows, w.causal, x["mask"])
-        kr = oracle.key_rows(x["q"][b, h], x["k"][b, h], x["v"][b, h], x["do"][b, h],
-                             w.scale, rows, w.causal, x["mask"])
-        ref = {**qr, **kr}
-        for n in OUTS:
-            g = got[n][b, h][torch.from_numpy(rows).to(device())].float().cpu().numpy()
-            e = tol_check(n, g, ref[n], w.dtype)
-            _say(f"  {name} head ({b},{h}) {n}: " +
-                 " ".join(f"{kk}={vv:.3e}" for kk, vv in e.items()))
+
+@pytest.mark.parametrize("N,d,dtype,causal,mk", NEG,
+                         ids=[f"N{a}-d{b}-{c}-{'causal' if e else 'dense'}-{f or 'nomask'}"
+                              for a, b, c, e, f in NEG])
+def test_negative_scale_against_oracle(N, d, dtype, causal, mk):
+    inp = W.random_inputs(1, 3, N, d, dtype, seed=N + 3 * d)
+    mask = W.random_block_mask(N, 0.6, seed=N + 1) if mk == "rand" else None
+    scale = -1.0 / math.sqrt(d)
+    _say(f"case scale={scale:.4f} N={N} d={d} {dtype} causal={causal} mask={mk}")
+    got = run_hip(inp, dtype, scale, causal, mask)
+    ref = oracle.forward_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, causal, mask)
+    check_all(got, ref, dtype, f"neg N={N}")
+
+
+@pytest.mark.parametrize("dtype,d,causal", [("bf16", 128, True), ("bf16", 64, False),
+                                            ("fp32", 64, True)])
+def test_negative_scale_is_positive_scale_on_negated_q(dtype, d, causal):
+    """scale * <Q, K> = (-scale) * <-Q, K> exactly, and the kernels apply a
+    negative scale by flipping the sign of Q (or of K in the dK/dV pass), so
+    the two calls give the same bits: O, LSE, dK, dV equal, dQ negated."""
+    inp = W.random_inputs(2, 2, 333, d, dtype, seed=31)
+    scale = 0.7 / math.sqrt(d)
+    a = run_hip(inp, dtype, -scale, causal)
+    b = run_hip(dict(inp, q=-inp["q"]), dtype, scale, causal)
+    for n in ("O", "LSE", "dK", "dV"):
+        assert np.array_equal(a[n], b[n]), n
+    assert np.array_equal(a["dQ"], -b["dQ"])
+
+
+# --------------------------------------------------------------------------
+# Non-finite inputs propagate to exactly the outputs they feed.
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,d,causal", [("bf16", 128, False), ("bf16", 64, True),
+                                            ("fp32", 128, True)])
+def test_nan_inputs_reach_only_the_outputs_they_feed(dtype, d, causal):
+    """A NaN row of Q (row i0) and a NaN row of dO (row i1):
+      * O and LSE are NaN exactly in row i0;
+      * dQ is NaN exactly in rows i0 and i1;
+      * dK, dV are NaN at every key kept by row i0 or i1; keys outside every
+        128-key tile those rows visit stay finite (inside a visited tile the
+        matrix products multiply the NaN row by zero weights, so a masked key
+        there may turn NaN as well);
+    and every finite output equals the oracle's on the same inputs with the
+    NaN rows set to zero (those rows do not feed the entries compared)."""
+    N = 512
+    inp = W.random_inputs(1, 2, N, d, dtype, seed=41)
+    mask = None if causal else W.random_block_mask(N, 0.5, seed=43)
+    i0, i1 = 200, 333
+    x = {n: t.copy() for n, t in inp.items()}
+    x["q"][0, 1, i0] = np.nan
+    x["do"][0, 1, i1] = np.nan
+    scale = 1 / math.sqrt(d)
+    got = run_hip(x, dtype, scale, causal, mask)
+    z = {n: t.copy() for n, t in inp.items()}
+    z["q"][0, 1, i0] = 0.0
+    z["do"][0, 1, i1] = 0.0
+    ref = oracle.forward_backward(z["q"], z["k"], z["v"], z["do"], scale, causal, mask)
+    keep = oracle.keep_matrix(N, N, causal, mask)
+    fed = keep[i0] | keep[i1]                       # keys fed by the NaN rows
+    tiles = np.zeros(N, bool)                       # keys of 128-tiles those rows visit
+    for i in (i0, i1):
+        for t in range(N // 128):
+            if keep[i, 128 * t:128 * t + 128].any():
+                tiles[128 * t:128 * t + 128] = True
+    rows = np.zeros(N, bool)
+    for name in OUTS:
+        g = got[name][0, 1]
+        bad = ~np.isfinite(g) if g.ndim == 1 else ~np.isfinite(g).all(axis=-1)
+        if name in ("O", "LSE"):
+            want = rows.copy(); want[i0] = True
+            assert np.array_equal(bad, want), name
+        elif name == "dQ":
+            want = rows.copy(); want[i0] = want[i1] = True
+            assert np.array_equal(bad, want), name
+        else:
+            assert bad[fed].all(), name
+            assert not bad[~tiles].any(), name
+            g = g[~tiles]
+        assert np.isfinite(got[name][0, 0]).all(), name       # the other head
+        ok = ~bad if name not in ("dK", "dV") else slice(None)
+        r = ref[name][0, 1] if name not in ("dK", "dV") else ref[name][0, 1][~tiles]
+        tol_check(name, g[ok], r[ok], dtype)
+        tol_check(name, got[name][0, 0], ref[name][0, 0], dtype)

@@ -268,10 +268,11 @@ def _loss(q, k, v, do, scale, causal, mask, mb):
     return float((o * do).sum())
 
 
+@pytest.mark.parametrize("scale", [0.7, -0.45])
 @pytest.mark.parametrize("N,d", [(1, 3), (5, 3), (16, 8)])
 @pytest.mark.parametrize("causal,use_mask", [(False, False), (True, False), (False, True),
                                              (True, True)])
-def test_gradients_match_finite_differences(N, d, causal, use_mask):
+def test_gradients_match_finite_differences(N, d, causal, use_mask, scale):
     q, k, v, do = _qkvdo(1, 1, N, d, seed=37 + N + d)
     mb = 4
     t = -(-N // mb)
@@ -279,7 +280,6 @@ def test_gradients_match_finite_differences(N, d, causal, use_mask):
     if use_mask:
         mask = (np.random.default_rng(41).random((t, t)) < 0.6).astype(np.uint8)
         mask[np.arange(t), np.arange(t)] = 1
-    scale = 0.7
     r = oracle.forward_backward(q, k, v, do, scale, causal, mask, mask_block=mb)
     h = 1e-6
     for name, x in (("dQ", q), ("dK", k), ("dV", v)):
@@ -314,6 +314,28 @@ def test_gradient_identities():
     o1, _ = oracle.forward(q, k, v, 0.35, False)
     o2, _ = oracle.forward(q, k + 0.5, v, 0.35, False)
     np.testing.assert_allclose(o2, o1, atol=1e-12)
+
+
+def test_negative_scale():
+    """Any finite scale: a negative one weights the keys by exp of minus the
+    dot product (scipy's softmax of the negated scores), and a large negative
+    scale picks the key with the smallest score."""
+    from scipy.special import logsumexp, softmax
+    q, k, v, do = _qkvdo(1, 2, 12, 5, seed=53)
+    o, lse = oracle.forward(q, k, v, -0.8, False)
+    for h in range(2):
+        s_ = -0.8 * q[0, h] @ k[0, h].T
+        np.testing.assert_allclose(o[0, h], softmax(s_, axis=1) @ v[0, h], atol=1e-13)
+        np.testing.assert_allclose(lse[0, h], logsumexp(s_, axis=1), atol=1e-13)
+    o_big, _ = oracle.forward(q, k, v, -1e4, False)
+    arg = np.argmin(q[0, 0] @ k[0, 0].T, axis=1)
+    np.testing.assert_allclose(o_big[0, 0], v[0, 0][arg], atol=1e-9)
+    # -scale with Q equals +scale with -Q (dQ changes sign)
+    a = oracle.forward_backward(q, k, v, do, -0.8, True)
+    b = oracle.forward_backward(-q, k, v, do, 0.8, True)
+    for n in ("O", "LSE", "dK", "dV"):
+        np.testing.assert_allclose(a[n], b[n], atol=1e-13)
+    np.testing.assert_allclose(a["dQ"], -b["dQ"], atol=1e-13)
 
 
 def test_scale_is_applied_to_scores():

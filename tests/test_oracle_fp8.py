@@ -158,3 +158,45 @@ def test_planted_mistakes_fail(monkeypatch):
                                                        good[0]).astype(np.uint8))
         with pytest.raises(AssertionError):
             test_rounding_is_nearest_with_ties_to_even()
+
+
+@pytest.mark.parametrize("shift", [8, 0, 3])
+def test_head_rows_equals_rows_of_the_full_results(shift):
+    """The row helper used by the full-size FP8 check is the full forward and
+    the full bound restricted to the sampled rows: masked, causal, several
+    heads, a large-logit key and a zero key block, every shift."""
+    rng = np.random.default_rng(5)
+    B, H, N, d, blk = 2, 3, 96, 16, 32
+    q, k, v = (rng.standard_normal((B, H, N, d)) for _ in range(3))
+    k[1, 2, 40] *= 20.0
+    k[0, 1, 64:96] = 0.0
+    q8, sq = fp8.quantize_rows(q, blk)
+    k8, sk = fp8.quantize_rows(k, blk)
+    vt8, sv = fp8.quantize_heads_transposed(v)
+    mask = np.array([[1, 0, 0], [1, 1, 0], [0, 1, 1]], np.uint8)
+    o, lse = fp8.forward(q8, k8, vt8, sq, sk, sv, 0.4, True, mask, blk)
+    bound = fp8.o_error_bound(q8, k8, vt8, sq, sk, sv, 0.4, True, mask, blk, shift=shift)
+    rows = np.array([0, 5, 31, 32, 50, 95])
+    for b in range(B):
+        for h in range(H):
+            r = fp8.head_rows(q8, k8, vt8, sq, sk, sv, b, h, rows, 0.4, True, mask, blk,
+                              shift=shift)
+            np.testing.assert_allclose(r["O"], o[b, h, rows], rtol=1e-13, atol=1e-15)
+            np.testing.assert_allclose(r["LSE"], lse[b, h, rows], rtol=1e-13)
+            np.testing.assert_allclose(r["bound"], bound[b, h, rows], rtol=1e-13, atol=0)
+
+
+def test_head_rows_subnormal_term_follows_shift():
+    """A planted fixed subnormal term (the shift-8 value at shift 0) breaks
+    the equality with o_error_bound."""
+    rng = np.random.default_rng(6)
+    q, k, v = (rng.standard_normal((1, 1, 64, 16)) for _ in range(3))
+    q8, sq = fp8.quantize_rows(q)
+    k8, sk = fp8.quantize_rows(k)
+    vt8, sv = fp8.quantize_heads_transposed(v)
+    rows = np.arange(64)
+    full0 = fp8.o_error_bound(q8, k8, vt8, sq, sk, sv, 0.3, True, shift=0)[0, 0]
+    good = fp8.head_rows(q8, k8, vt8, sq, sk, sv, 0, 0, rows, 0.3, True, shift=0)["bound"]
+    wrong = fp8.head_rows(q8, k8, vt8, sq, sk, sv, 0, 0, rows, 0.3, True, shift=8)["bound"]
+    np.testing.assert_allclose(good, full0, rtol=1e-13)
+    assert not np.allclose(wrong, full0, rtol=1e-6)
