@@ -98,5 +98,25 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     return LIB
 
 
+PROBE_SRC = os.path.join(ROOT, "tests", "gpu_probe", "mfma_rounding_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "tests", "gpu_probe", "libfa_probe.so")
+
+
+def build_test_probe(verbose: bool = False) -> str:
+    """Test support, not part of libfa.so: the one-wave matrix-instruction
+    probe the GPU tests use to check the accumulation model of the FP8 and
+    bf16 instructions (tests/gpu_probe)."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc(), "-shared", PROBE_SRC, "-o", tmp] + common_flags()
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB}")
+    return PROBE_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True, extra=sys.argv[1:])
+    build_test_probe(verbose=True)

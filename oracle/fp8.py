@@ -24,6 +24,14 @@ format of the gfx950 matrix cores):
     Qd, Kd, Vd the dequantized tensors.  The GPU also rounds the probabilities
     to E4M3 before the P V product (as FlashAttention-3 does); that error is
     bounded in ``o_error_bound``.
+  * The FP8 matrix instruction does not add its 64 products in full fp32
+    precision (measured on gfx950 with a one-wave probe, and re-checked by the
+    GPU tests): it returns C + sum_k p_k up to an error of a few units of
+    2^(E - 14), E = floor(log2 max(|C|, max_k |p_k|)) -- at most 8.8 such units
+    over 40,960 random sums, unbiased for products of mixed sign.  The scores,
+    and so LSE, carry that error; ``lse_allowance`` bounds it with 16 units
+    per instruction (about twice the largest seen).  Products of two E4M3
+    values are exact, so the scores' only other error is this one.
 """
 
 from __future__ import annotations
@@ -163,3 +171,58 @@ def head_rows(q8, k8, vt8, sq, sk, sv, b: int, h: int, rows, scale: float,
     av = np.abs(decode(vt8[b, h]).T)
     bound = float(sv[b, h]) * (2.0 ** -4 * (p @ av) + 2.0 ** (-10 - shift) * (keep @ av))
     return {"O": o, "LSE": lse, "bound": bound}
+
+
+# Accumulation model of the FP8 matrix instruction (module docstring): the
+# result is within UNITS * 2^(E - WINDOW) of the exact C + sum of products.
+MFMA_WINDOW = 14
+MFMA_UNITS = 16.0
+MFMA_GROUP = 64          # products per instruction and output element
+
+
+def _pow2_floor(x):
+    """2^floor(log2 x) for x > 0, 0 for x == 0."""
+    x = np.asarray(x, np.float64)
+    out = np.zeros_like(x)
+    pos = x > 0
+    out[pos] = np.exp2(np.floor(np.log2(x[pos])))
+    return out
+
+
+def lse_allowance(q8, k8, sq, sk, scale: float, causal: bool = False, block_mask=None,
+                  mask_block: int = MASK_BLOCK, units: float = MFMA_UNITS,
+                  window: int = MFMA_WINDOW):
+    """Per-row bound [B, H, N] on |LSE_gpu - LSE| that the FP8 instruction's
+    accumulation allows.
+
+    Score s_ij = scale sQ_i sK_j S_ij with S_ij = sum_k a_ik b_jk over the
+    decoded codes, formed by d / 64 instructions in order; instruction g adds
+    the products of its 64 dimensions to the partial sum C_g of the earlier
+    ones, with an error of at most units * 2^(E_g - window),
+    E_g = floor(log2 max(|C_g|, max_k |a_ik b_jk|)) (products bounded by the
+    row maxima of the codes in that group).  LSE_i = ln sum_j exp(s_ij) moves
+    by at most the largest change of a kept score, so the allowance of row i
+    is max over kept j of |scale| sQ_i sK_j sum_g units 2^(E_g - window).
+    (A row that keeps nothing has no LSE to move: allowance 0.)
+    """
+    from .attention import keep_rows
+    a_all, b_all = decode(q8), decode(k8)
+    B, H, N, d = a_all.shape
+    rows_blk = np.arange(N) // mask_block
+    out = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            a, bk = a_all[b, h], b_all[b, h]
+            fq = abs(scale) * np.asarray(sq, np.float64)[b, h][rows_blk]        # per query row
+            fk = np.asarray(sk, np.float64)[b, h][rows_blk]                      # per key row
+            partial = np.zeros((N, N))
+            err = np.zeros((N, N))
+            for g0 in range(0, d, MFMA_GROUP):
+                ga, gb = a[:, g0:g0 + MFMA_GROUP], bk[:, g0:g0 + MFMA_GROUP]
+                pmax = np.abs(ga).max(1)[:, None] * np.abs(gb).max(1)[None, :]
+                err += units * _pow2_floor(np.maximum(np.abs(partial), pmax)) * 2.0 ** -window
+                partial = partial + ga @ gb.T
+            ds = fq[:, None] * fk[None, :] * err
+            keep = keep_rows(np.arange(N), N, causal, block_mask, mask_block)
+            out[b, h] = np.where(keep, ds, 0.0).max(1)
+    return out

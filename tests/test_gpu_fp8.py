@@ -46,12 +46,19 @@ def _run(qz, scale, causal, mask):
     return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-def _check(o, lse, o_ref, lse_ref, bound, label):
+def _check(o, lse, o_ref, lse_ref, bound, label, allow=None):
+    """O within the probability-rounding bound; LSE within 1e-4 max(1, |LSE|)
+    plus ``allow``, the score error the FP8 instruction's accumulation allows
+    (oracle.fp8.lse_allowance; its model is checked by test_instruction_*)."""
     inf = np.isneginf(lse_ref)
     assert np.array_equal(np.isneginf(lse), inf), f"{label}: -inf pattern of LSE"
     lerr = np.abs(lse[~inf] - lse_ref[~inf])
-    assert np.all(lerr <= 1e-4 * np.maximum(1.0, np.abs(lse_ref[~inf]))), \
-        f"{label}: LSE error {lerr.max():.3e}"
+    plain = 1e-4 * np.maximum(1.0, np.abs(lse_ref[~inf]))
+    extra = 0.0 if allow is None else allow[~inf]
+    over = int((lerr > plain).sum())
+    _say(f"  {label}: LSE rows over the plain 1e-4 bar: {over} of {lerr.size}; worst "
+         f"error / (bar + allowance) {(lerr / (plain + extra)).max() if lerr.size else 0:.3f}")
+    assert np.all(lerr <= plain + extra), f"{label}: LSE error {lerr.max():.3e}"
     assert np.isfinite(o).all()
     err = np.abs(o - o_ref)
     lim = bound + 2.0 ** -8 * np.abs(o_ref) + 1e-6
@@ -89,7 +96,8 @@ def test_small_against_oracle(B, H, N, d, causal, mk):
     args = (qz["q8"], qz["k8"], qz["vt8"], qz["sq"], qz["sk"], qz["sv"], scale, causal, mask)
     o_ref, lse_ref = OF.forward(*args)
     bound = OF.o_error_bound(*args)
-    _check(o, lse, o_ref, lse_ref, bound, "whole output")
+    allow = OF.lse_allowance(qz["q8"], qz["k8"], qz["sq"], qz["sk"], scale, causal, mask)
+    _check(o, lse, o_ref, lse_ref, bound, "whole output", allow)
 
 
 def test_negative_scale():
@@ -101,4 +109,100 @@ def test_negative_scale():
     o, lse = _run(qz, -0.1, True, None)
     args = (qz["q8"], qz["k8"], qz["vt8"], qz["sq"], qz["sk"], qz["sv"], -0.1, True, None)
     o_ref, lse_ref = OF.forward(*args)
-    _check(o, lse, o_ref, lse_ref, OF.o_error_bound(*args), "negative scale")
+    allow = OF.lse_allowance(qz["q8"], qz["k8"], qz["sq"], qz["sk"], -0.1, True, None)
+    _check(o, lse, o_ref, lse_ref, OF.o_error_bound(*args), "negative scale", allow)
+
+
+
+# --------------------------------------------------------------------------
+# The accumulation model of the matrix instructions (oracle/fp8.py): the FP8
+# instruction returns C + sum of its 64 products within MFMA_UNITS units of
+# 2^(E - 14), E = floor(log2 max(|C|, max |p|)); the bf16 instruction within
+# fp32 rounding.  Checked here with the one-wave probe (tests/gpu_probe).
+# --------------------------------------------------------------------------
+
+def _probe_lib():
+    import ctypes
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "gpu_probe",
+                        "libfa_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} missing: build it first (__graft_entry__.build())")
+    return ctypes.CDLL(path)
+
+
+def _probe(lib, fn, A, Bt, C0):
+    import ctypes
+    tA, tB = _dev(A), _dev(Bt)
+    tC0 = _dev(np.asarray(C0, np.float32))
+    tC = torch.empty(1024, dtype=torch.float32, device=device())
+    assert getattr(lib, fn)(ctypes.c_void_p(tA.data_ptr()), ctypes.c_void_p(tB.data_ptr()),
+                            ctypes.c_void_p(tC0.data_ptr()), ctypes.c_void_p(tC.data_ptr())) == 0
+    return tC.cpu().numpy().reshape(32, 32).astype(np.float64)
+
+
+def test_instruction_model_fp8():
+    """Random E4M3 sums (full-range codes, normal data, one large key among
+    small ones, same-sign products, large accumulators): every result lies
+    within MFMA_UNITS units of 2^(E - 14) of the exact sum, and the small
+    products of a sum with one large product are dropped below 2^(E - 14)
+    (the model is not slack: fp32 addition would keep them)."""
+    lib = _probe_lib()
+    rng = np.random.default_rng(12)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    worst = 0.0
+    for t in range(48):
+        kind = t % 6
+        if kind == 0:
+            A, Bt = rng.choice(finite, (32, 64)), rng.choice(finite, (32, 64))
+        elif kind == 1:
+            A, Bt = (OF.encode(rng.standard_normal((32, 64)) * 100) for _ in range(2))
+        elif kind == 2:
+            A = OF.encode(rng.standard_normal((32, 64)) * 100)
+            Bt = OF.encode(rng.standard_normal((32, 64)) * 5)
+            Bt[:, ::13] = OF.encode(rng.standard_normal((32, 5)) * 150)
+        elif kind == 3:
+            A, Bt = (OF.encode(np.abs(rng.standard_normal((32, 64))) * 50) for _ in range(2))
+        else:
+            A, Bt = (OF.encode(rng.standard_normal((32, 64)) * 100) for _ in range(2))
+        A, Bt = np.asarray(A, np.uint8), np.asarray(Bt, np.uint8)
+        C0 = np.zeros((32, 32)) if kind < 4 else \
+            (rng.standard_normal((32, 32)) * (1e4 if kind == 4 else 1e6)).astype(np.float32)
+        C = _probe(lib, "fa_probe_fp8", A, Bt, C0)
+        P = OF.decode(A)[:, None, :] * OF.decode(Bt)[None, :, :]
+        exact = np.asarray(C0, np.float64) + P.sum(-1)
+        E = np.floor(np.log2(np.maximum(np.abs(P).max(-1), np.abs(np.asarray(C0, np.float64)))))
+        units = np.abs(C - exact) / 2.0 ** (E - OF.MFMA_WINDOW)
+        worst = max(worst, float(units.max()))
+    _say(f"  FP8 instruction: worst error {worst:.2f} units of 2^(E-14) "
+         f"(allowance {OF.MFMA_UNITS:.0f})")
+    assert worst <= OF.MFMA_UNITS
+    # one product of 448 * 448 (E = 17) plus one of 2^2: dropped; plus 2^3: kept
+    A = np.zeros((32, 64), np.uint8); Bt = np.zeros((32, 64), np.uint8)
+    A[:, 0] = Bt[:, 0] = 0x7E
+    A[:16, 1] = OF.encode(4.0)[()]
+    A[16:, 1] = OF.encode(8.0)[()]
+    Bt[:, 1] = OF.encode(1.0)[()]
+    C = _probe(lib, "fa_probe_fp8", A, Bt, np.zeros((32, 32)))
+    assert np.all(C[:16] == 448.0 * 448.0) and np.all(C[16:] == 448.0 * 448.0 + 8.0)
+
+
+def test_instruction_model_bf16():
+    """The bf16 instruction adds its 16 products to C in fp32 precision."""
+    lib = _probe_lib()
+    rng = np.random.default_rng(13)
+    worst = 0.0
+    for scale_c in (0.0, 1e3):
+        a = torch.from_numpy(rng.standard_normal((32, 16)).astype(np.float32)).to(torch.bfloat16)
+        b = torch.from_numpy(rng.standard_normal((32, 16)).astype(np.float32)).to(torch.bfloat16)
+        C0 = (rng.standard_normal((32, 32)) * scale_c).astype(np.float32)
+        C = _probe(lib, "fa_probe_bf16", a.view(torch.int16).numpy(),
+                   b.view(torch.int16).numpy(), C0)
+        A64 = a.float().numpy().astype(np.float64)
+        B64 = b.float().numpy().astype(np.float64)
+        P = A64[:, None, :] * B64[None, :, :]
+        exact = C0.astype(np.float64) + P.sum(-1)
+        scale = np.abs(P).sum(-1) + np.abs(C0)
+        worst = max(worst, float((np.abs(C - exact) / scale).max()))
+    _say(f"  bf16 instruction: worst error / (|C| + sum|p|) {worst:.2e}")
+    assert worst <= 17 * 2.0 ** -24

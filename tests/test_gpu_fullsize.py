@@ -76,10 +76,14 @@ def _compare(name, got, ref, w, label, literal):
         _say(f"  {label} LSE: max-abs {e['max_abs']:.3e}")
         return
     fl = _floor(ref)
-    heads = got.reshape(-1, *got.shape[-2:]), ref.reshape(-1, *ref.shape[-2:])
-    per_head = [float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
-                for a, b in zip(*heads)]
-    _say(f"  {label} {name}: rel-Fro {e['rel_fro']:.3e} (worst head {max(per_head):.3e}), "
+    if got.ndim == 4:
+        heads = got.reshape(-1, *got.shape[-2:]), ref.reshape(-1, *ref.shape[-2:])
+        per_head = [float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+                    for a, b in zip(*heads)]
+        worst = f" (worst head {max(per_head):.3e})"
+    else:
+        worst = ""
+    _say(f"  {label} {name}: rel-Fro {e['rel_fro']:.3e}{worst}, "
          f"max-abs {e['max_abs']:.3e} (bf16 floor {fl:.3e}, max|ref| {e['ref_max']:.2f})")
     if literal:
         assert e["max_abs"] <= 2e-2, f"{name}: max-abs {e['max_abs']:.3e} > 2e-2 (literal)"
@@ -129,14 +133,16 @@ def test_verylong_rows_of_every_head():
             acc[n][1].append(ref[n])
         _say(f"  head {h}: {len(rows)} rows")
     for n in OUTS:
-        g, r = np.stack(acc[n][0]), np.stack(acc[n][1])
+        g, r = np.concatenate(acc[n][0]), np.concatenate(acc[n][1])
         _compare(n, g, r, w, "verylong (sampled rows)", True)
 
 
 def test_long_fp8_whole_output():
     """The long-context shape quantized to FP8 (the FP8 forward the
     benchmark times): every head against exact attention on the dequantized
-    inputs, within the probability-rounding bound of the oracle."""
+    inputs: O within the probability-rounding bound of the oracle, LSE within
+    1e-4 max(1, |LSE|) plus the FP8 instruction's score-accumulation
+    allowance (oracle.fp8.lse_allowance)."""
     w = W.WORKLOADS["long_fp8"]
     x = W.make_inputs(w)
     qz = W.quantize_fp8(x["q"], x["k"], x["v"])
@@ -151,5 +157,6 @@ def test_long_fp8_whole_output():
     args = (qz["q8"], qz["k8"], qz["vt8"], qz["sq"], qz["sk"], qz["sv"], w.scale, w.causal)
     o_ref, lse_ref = OF.forward(*args)
     bound = OF.o_error_bound(*args)
+    allow = OF.lse_allowance(qz["q8"], qz["k8"], qz["sq"], qz["sk"], w.scale, w.causal)
     fp8_check(o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
-              o_ref, lse_ref, bound, "long_fp8, all 32 heads")
+              o_ref, lse_ref, bound, "long_fp8, all 32 heads", allow)

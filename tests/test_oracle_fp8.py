@@ -200,3 +200,67 @@ def test_head_rows_subnormal_term_follows_shift():
     wrong = fp8.head_rows(q8, k8, vt8, sq, sk, sv, 0, 0, rows, 0.3, True, shift=8)["bound"]
     np.testing.assert_allclose(good, full0, rtol=1e-13)
     assert not np.allclose(wrong, full0, rtol=1e-6)
+
+
+def _lse_with_instruction_errors(q8, k8, sq, sk, scale, causal, sign, units=fp8.MFMA_UNITS,
+                                 window=fp8.MFMA_WINDOW):
+    """LSE from scores formed instruction by instruction, each instruction's
+    result pushed by sign * units * 2^(E - window) (the model's extreme),
+    written out with loops over rows, keys and 64-wide groups."""
+    a, b = fp8.decode(q8), fp8.decode(k8)
+    B, H, N, d = a.shape
+    lse = np.empty((B, H, N))
+    for bb in range(B):
+        for h in range(H):
+            for i in range(N):
+                s = np.full(N, -np.inf)
+                for j in range(N):
+                    if causal and j > i:
+                        continue
+                    c = 0.0
+                    for g0 in range(0, d, 64):
+                        p = a[bb, h, i, g0:g0 + 64] * b[bb, h, j, g0:g0 + 64]
+                        m = max(abs(c), float(np.abs(p).max()))
+                        e = 2.0 ** (math.floor(math.log2(m)) - window) if m > 0 else 0.0
+                        c = c + float(p.sum()) + sign * units * e
+                    s[j] = scale * float(sq[bb, h, i // 128]) * float(sk[bb, h, j // 128]) * c
+                mx = s.max()
+                lse[bb, h, i] = mx + math.log(np.exp(s - mx).sum())
+    return lse
+
+
+@pytest.mark.parametrize("d,causal,scale", [(64, False, 0.3), (128, True, -0.2)])
+def test_lse_allowance_covers_the_instruction_model(d, causal, scale):
+    """Scores pushed to the model's extreme in either direction move LSE by
+    at most the allowance (equality when every kept score moves by the same
+    amount), on inputs with a large-logit key; a narrower window (a planted
+    mistake) gives an allowance the same extreme exceeds."""
+    rng = np.random.default_rng(8)
+    q, k = (rng.standard_normal((1, 2, 20, d)) for _ in range(2))
+    k[0, 1, 3] *= 20.0
+    q8, sq = fp8.quantize_rows(q)
+    k8, sk = fp8.quantize_rows(k)
+    _, lse = fp8.forward(q8, k8, fp8.quantize_heads_transposed(q)[0], sq, sk,
+                         np.ones((1, 2), np.float32), scale, causal)
+    allow = fp8.lse_allowance(q8, k8, sq, sk, scale, causal)
+    assert np.all(allow > 0)
+    worst = 0.0
+    for sign in (1.0, -1.0):
+        moved = _lse_with_instruction_errors(q8, k8, sq, sk, scale, causal, sign)
+        dl = np.abs(moved - lse)
+        assert np.all(dl <= allow * (1 + 1e-9) + 1e-12)
+        worst = max(worst, float((dl / allow).max()))
+    assert worst > 0.3                     # the allowance is not vacuous
+    narrow = fp8.lse_allowance(q8, k8, sq, sk, scale, causal, window=fp8.MFMA_WINDOW + 4)
+    moved = _lse_with_instruction_errors(q8, k8, sq, sk, scale, causal, 1.0)
+    assert np.any(np.abs(moved - lse) > narrow * (1 + 1e-9))
+
+
+def test_lse_allowance_zero_codes_and_masked_rows():
+    q8 = np.zeros((1, 1, 8, 64), np.uint8)
+    k8 = fp8.encode(np.random.default_rng(9).standard_normal((1, 1, 8, 64)))
+    ones = np.ones((1, 1, 1), np.float32)
+    assert np.all(fp8.lse_allowance(q8, k8, ones, ones, 0.5) == 0.0)   # all products zero
+    mask = np.zeros((1, 1), np.uint8)                                  # nothing kept
+    q8 = fp8.encode(np.ones((1, 1, 8, 64)))
+    assert np.all(fp8.lse_allowance(q8, k8, ones, ones, 0.5, block_mask=mask) == 0.0)
