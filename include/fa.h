@@ -72,6 +72,8 @@ typedef enum {
   FA_ERR_ARG = 8,        /* scale not finite, dropout_p outside [0, 1), or
                             num_splits outside [0, 1024] */
   FA_ERR_ALIAS = 9,      /* an output overlaps an input or another output */
+  FA_ERR_SCRATCH = 10,   /* fa_bwd_static: the sizes need more than the
+                            library's static scratch holds */
   /* Not statuses: these two give the enum the whole range of int, so that any
      int a caller passes or compares is a valid value of the type. */
   FA_STATUS_INT_MIN_ = -2147483647 - 1,
@@ -173,6 +175,27 @@ fa_status fa_bwd_dq(const void* Q, const void* K, const void* V, const void* dO,
                     const float* LSE, void* dQ, int B, int H, int N, int d, float scale,
                     int causal, const unsigned char* block_mask, fa_dtype dtype,
                     const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_bwd_static -- fa_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same gradients, the same kernels and checks, but no
+ * workspace argument.  The row term D goes to a static device array of
+ * FA_STATIC_SCRATCH_BYTES bytes that the library holds on every GPU it runs
+ * on until the process ends; the call allocates nothing.  It needs
+ * 4 * B * H * N <= FA_STATIC_SCRATCH_BYTES (else FA_ERR_SCRATCH, nothing
+ * enqueued).  The device address of the array is looked up on the first call
+ * on each device (with that device current); a failed lookup gives
+ * FA_ERR_LAUNCH.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (on different streams without ordering between them)
+ * race on it.  Its contents need no initialisation (every value of D is
+ * written before it is read).
+ */
+#define FA_STATIC_SCRATCH_BYTES 4194304
+fa_status fa_bwd_static(const void* Q, const void* K, const void* V, const void* O,
+                        const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                        int B, int H, int N, int d, float scale, int causal,
+                        const unsigned char* block_mask, fa_dtype dtype, void* stream);
 
 /*
  * fa_fwd_dropout / fa_bwd_dropout -- fa_fwd and fa_bwd with dropout on the

@@ -23,7 +23,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfa.so")
 ARCH = "gfx950"
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_fwd_fp8.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_fwd_fp8.hip",
+           "fa_static.hip"]
 
 
 def hipcc() -> str:

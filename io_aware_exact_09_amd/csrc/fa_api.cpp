@@ -278,6 +278,24 @@ FA_EXPORT fa_status fa_bwd(const void* Q, const void* K, const void* V, const vo
                   dtype, workspace, workspace_bytes, fa::Dropout{}, stream);
 }
 
+FA_EXPORT fa_status fa_bwd_static(const void* Q, const void* K, const void* V, const void* O,
+                                  const void* dO, const float* LSE, void* dQ, void* dK,
+                                  void* dV, int B, int H, int N, int d, float scale, int causal,
+                                  const unsigned char* block_mask, fa_dtype dtype,
+                                  void* stream) {
+  // The argument checks of fa_bwd come first, then the size limit, then the
+  // (once per device) lookup of the static array's device address.
+  FA_TRY(check_buffers({{Q, 0, 0}, {K, 0, 0}, {V, 0, 0}, {O, 0, 0}, {dO, 0, 0}, {LSE, 0, 0}},
+                       {{dQ, 0, 0}, {dK, 0, 0}, {dV, 0, 0}}));
+  const Shape s{B, H, N, d, dtype};
+  FA_TRY(check_shape(s, scale));
+  if (s.row_bytes() > (uintptr_t)FA_STATIC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (fa::static_scratch(&ws) != hipSuccess) return FA_ERR_LAUNCH;
+  return bwd_impl(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, H, N, d, scale, causal, block_mask,
+                  dtype, ws, FA_STATIC_SCRATCH_BYTES, fa::Dropout{}, stream);
+}
+
 FA_EXPORT fa_status fa_bwd_dropout(const void* Q, const void* K, const void* V, const void* O,
                                    const void* dO, const float* LSE, void* dQ, void* dK,
                                    void* dV, int B, int H, int N, int d, float scale, int causal,
@@ -515,6 +533,10 @@ FA_EXPORT const char* fa_status_str(fa_status s) {
     case FA_ERR_ARG:
       return "scale must be finite; dropout probability in [0, 1); num_splits in [0, 1024]";
     case FA_ERR_ALIAS: return "an output overlaps an input or another output";
+    case FA_ERR_SCRATCH:
+      return "the sizes need more than the library's static scratch (FA_STATIC_SCRATCH_BYTES)";
+    case FA_STATUS_INT_MIN_:
+    case FA_STATUS_INT_MAX_: break;
   }
   return "unknown status";
 }

@@ -59,6 +59,10 @@ struct Fp8FwdArgs {
   hipStream_t stream;
 };
 
+// Device address of the library's static scratch (FA_STATIC_SCRATCH_BYTES
+// bytes) on the current device, looked up once per device (fa_static.hip).
+hipError_t static_scratch(void** ptr);
+
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_fwd_fp8(const Fp8FwdArgs& a);
 hipError_t launch_bwd_preprocess(const BwdArgs& a);

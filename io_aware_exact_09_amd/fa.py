@@ -30,8 +30,9 @@ MASK_BLOCK = 128
 STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEAD_DIM",
     4: "FA_ERR_DTYPE", 5: "FA_ERR_ALIGN", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_LAUNCH",
-    8: "FA_ERR_ARG", 9: "FA_ERR_ALIAS",
+    8: "FA_ERR_ARG", 9: "FA_ERR_ALIAS", 10: "FA_ERR_SCRATCH",
 }
+STATIC_SCRATCH_BYTES = 4194304     # FA_STATIC_SCRATCH_BYTES of include/fa.h
 
 
 class FAError(RuntimeError):
@@ -63,6 +64,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i,
                                vp, sz, vp]
         lib.fa_bwd.restype = i
+        lib.fa_bwd_static.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp,
+                                      i, vp]
+        lib.fa_bwd_static.restype = i
         lib.fa_bwd_preprocess.argtypes = [vp, vp, i, i, i, i, i, vp, sz, vp]
         lib.fa_bwd_preprocess.restype = i
         lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz,
@@ -196,6 +200,22 @@ def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = False,
                     _ptr(block_mask), _dtype_code(q), _ptr(workspace), wbytes,
                     _stream(stream))
     _check(st, "fa_bwd")
+
+
+def fa_bwd_static(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = False,
+                  block_mask=None, stream=None) -> None:
+    """fa_bwd without a workspace: D goes to the library's static device
+    scratch, so the call allocates nothing (here or in the library).  Needs
+    4 * B * H * N <= STATIC_SCRATCH_BYTES; calls that overlap on one GPU race
+    on the shared scratch."""
+    lib = load_library()
+    _check_tensors(q, dict(q=q, k=k, v=v, o=o, do=do, lse=lse, dq=dq, dk=dk, dv=dv))
+    _mask_ok(q, block_mask)
+    B, H, N, d = q.shape
+    st = lib.fa_bwd_static(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                           _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
+                           _ptr(block_mask), _dtype_code(q), _stream(stream))
+    _check(st, "fa_bwd_static")
 
 
 def fa_fwd_dropout(q, k, v, o, lse, scale: float, dropout_p: float, seed: int,

@@ -19,6 +19,7 @@
 
 namespace fa {
 extern int g_launches;
+extern int g_scratch_lookups;
 extern FwdArgs g_fwd;
 extern BwdArgs g_bwd;
 extern Fp8FwdArgs g_fp8;
@@ -155,6 +156,25 @@ static void backward_cases() {
                                  nullptr, (fa_dtype)3, P(9), need, nullptr));
 }
 
+static void static_scratch_cases() {
+  const int rows = FA_STATIC_SCRATCH_BYTES / 4;
+  ACCEPT(3, fa_bwd_static(P(0), P(1), P(2), P(3), P(4), F(5), P(6), P(7), P(8), 2, 16, 4096,
+                          128, 0.1f, 1, nullptr, FA_BF16, nullptr));
+  EXPECT((uintptr_t)fa::g_bwd.delta == 0x7e0000000000ull && fa::g_bwd.gsplit == 1);
+  ACCEPT(3, fa_bwd_static(P(0), P(1), P(2), P(3), P(4), F(5), P(6), P(7), P(8), 1, 1, rows, 64,
+                          -0.1f, 0, nullptr, FA_FP32, nullptr));
+  const int looked = fa::g_scratch_lookups;
+  REJECT(FA_ERR_SCRATCH, fa_bwd_static(P(0), P(1), P(2), P(3), P(4), F(5), P(6), P(7), P(8), 1,
+                                       1, rows + 1, 64, 0.1f, 0, nullptr, FA_BF16, nullptr));
+  REJECT(FA_ERR_SHAPE, fa_bwd_static(P(0), P(1), P(2), P(3), P(4), F(5), P(6), P(7), P(8), 0, 1,
+                                     128, 64, 0.1f, 0, nullptr, FA_BF16, nullptr));
+  REJECT(FA_ERR_NULL, fa_bwd_static(P(0), P(1), P(2), P(3), nullptr, F(5), P(6), P(7), P(8), 1,
+                                    1, 128, 64, 0.1f, 0, nullptr, FA_BF16, nullptr));
+  EXPECT(fa::g_scratch_lookups == looked);      // rejected calls never look the buffer up
+  REJECT(FA_ERR_ALIAS, fa_bwd_static(P(0), P(1), P(2), P(3), P(4), F(5), P(6), P(6, 64), P(8),
+                                     1, 1, 128, 64, 0.1f, 0, nullptr, FA_BF16, nullptr));
+}
+
 static void fp8_cases() {
   ACCEPT(1, fa_fwd_fp8(P(0), P(1), P(2), F(3), F(4), F(5), P(6), F(7), 2, 16, 4096, 128, 0.1f,
                        1, nullptr, nullptr));
@@ -198,7 +218,7 @@ static void decode_cases() {
 }
 
 static void status_cases() {
-  for (int s = 0; s <= 9; ++s) {
+  for (int s = 0; s <= 10; ++s) {
     const char* str = fa_status_str((fa_status)s);
     EXPECT(str != nullptr && std::strcmp(str, "unknown status") != 0);
   }
@@ -209,6 +229,7 @@ static void status_cases() {
 int main() {
   forward_cases();
   backward_cases();
+  static_scratch_cases();
   fp8_cases();
   decode_cases();
   status_cases();

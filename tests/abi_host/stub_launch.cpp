@@ -20,4 +20,12 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a) { ++g_launches; g_bwd = a; return h
 hipError_t launch_bwd_dq(const BwdArgs& a) { ++g_launches; g_bwd = a; return hipSuccess; }
 hipError_t launch_decode(const DecodeArgs& a) { ++g_launches; g_dec = a; return hipSuccess; }
 
+// The static scratch's device address: a fixed fake address here.
+int g_scratch_lookups = 0;
+hipError_t static_scratch(void** ptr) {
+  ++g_scratch_lookups;
+  *ptr = reinterpret_cast<void*>(0x7e0000000000ull);
+  return hipSuccess;
+}
+
 }  // namespace fa

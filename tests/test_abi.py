@@ -33,7 +33,8 @@ def test_header_symbols_are_exported(lib):
                           "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
                           "fa_fwd_dropout", "fa_bwd_dropout", "fa_decode", "fa_fwd_gqa",
                           "fa_bwd_gqa", "fa_fwd_fp8", "fa_bwd_gqa_workspace_bytes",
-                          "fa_decode_num_splits", "fa_decode_workspace_bytes"}
+                          "fa_decode_num_splits", "fa_decode_workspace_bytes",
+                          "fa_bwd_static"}
     out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -308,3 +309,27 @@ def test_head_bytes_fit_32_bit_offsets(lib, N, dtype, ok):
 ])
 def test_decode_cache_head_fits_32_bit_offsets(lib, Nkv, dtype, ok):
     assert dec(lib, Nkv=Nkv, dtype=dtype, ns=1, q=p(0, 8)) == (5 if ok else 2)
+
+
+def test_static_scratch_entry_point_validation(lib):
+    """fa_bwd_static: the checks of fa_bwd, then the static scratch limit
+    (4 * B * H * N bytes of D must fit FA_STATIC_SCRATCH_BYTES); every call
+    below stops before the device is touched."""
+    def call(**kw):
+        a = dict(q=p(0), k=p(1), v=p(2), o=p(3), do=p(4), lse=p(5), dq=p(6), dk=p(7), dv=p(8),
+                 B=1, H=2, N=128, d=64, scale=0.125, causal=0, mask=None, dtype=BF16)
+        a.update(kw)
+        return lib.fa_bwd_static(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"],
+                                 a["dk"], a["dv"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                                 a["causal"], a["mask"], a["dtype"], None)
+    assert call(q=None) == 1
+    assert call(N=0) == 2
+    assert call(d=96) == 3
+    assert call(dtype=5) == 4
+    assert call(scale=float("nan")) == 8
+    rows = fa.STATIC_SCRATCH_BYTES // 4
+    assert call(B=1, H=1, N=rows + 1) == 10             # one row more than the scratch holds
+    assert call(B=2, H=16, N=rows // 16) == 10
+    assert "static scratch" in fa.status_str(10)
+    text = open(fa.HEADER_PATH).read()
+    assert f"#define FA_STATIC_SCRATCH_BYTES {fa.STATIC_SCRATCH_BYTES}" in text
