@@ -4,9 +4,15 @@
 
 A step is one pass of the whole hot path over one batch: fa_fwd, then the
 three backward phases (D preprocess, dK/dV pass, dQ pass), on torch's current
-stream, inputs resident in HBM.  W untimed warm-up steps, then exactly K timed
-steps bracketed by torch.cuda.synchronize(); each kernel is also bracketed by
-HIP events on the same stream for per-kernel durations.  Prints ONE JSON line.
+stream, inputs resident in HBM.  W untimed warm-up steps; then the secondary
+measurements (K steps without cache eviction, "warm", and the two-stream steps);
+then exactly K timed steps bracketed by torch.cuda.synchronize(), the headline.
+Before each of those (outside its HIP events) a 512 MiB device write evicts L2
+and the 256 MB Infinity Cache, so every timed step starts with its inputs in
+HBM only; each kernel of the step is bracketed by HIP events on the same
+stream.  The headline is the median step time of those K steps, taken last
+because the GPU's clocks need a few tens of steps of sustained work to settle.
+Prints ONE JSON line.
 
 Workloads are seeded synthetic inputs with the shapes of the FlashAttention
 reading guide's training workloads (io_aware_exact_09_amd/workloads.py); the
@@ -16,20 +22,23 @@ d = 128 shape the throughput target is stated for.
 Throughput uses algorithmic FLOPs (4 d per kept pair forward, 10 d backward;
 causal and block-sparse skipping excluded, the dQ pass's recomputation not
 counted).  The roofline object is for the kernel with the largest share of the
-step; peak is the published MI355X dense bf16 MFMA rate, 2.5 PFLOP/s (fp32
-MFMA 157.3 TFLOP/s for fp32 workloads).
+step, with its average launch time over the K timed steps; peak is the
+published MI355X dense bf16 MFMA rate, 2.5 PFLOP/s (fp32 MFMA 157.3 TFLOP/s
+for fp32 workloads).
 
 The cpu_baseline leg times the CPU fp64 oracle on a bounded sample of the same
 workload (whole heads, about 10-30 s) on this host's cores.  Secondary fields:
-cold_cache (steps after a 512 MiB write that evicts the caches) and
-two_stream_step (the dK/dV and dQ passes on two streams through the phase
-entry points; the headline step is fa_bwd's single stream).
+warm (the steps without the eviction) and two_stream_step (the dK/dV and dQ
+passes on two streams through the phase entry points; the headline step is
+fa_bwd's single stream).
 
 Decode workloads (--workload decode | decode_mix | decode_spec): a step is one
 fa_decode call over the whole batch (64 sequences, 8K cache, 32 query heads
 over 8 cache heads); value and roofline are algorithmic HBM bytes (visible
 cache rows of K and V once, Q, O, LSE) per second against 8 TB/s, with the HIP
-event pair around the call (its chunk kernel and the merge kernel).
+event pair around the call (its chunk kernel and the merge kernel).  FP8
+(--workload long_fp8): a step is one fa_fwd_fp8 call.  Both use the same
+protocol (evicted caches, median headline, warm secondary).
 """
 
 from __future__ import annotations
@@ -101,22 +110,56 @@ def copy_probe(args, dev):
     del src, dst
 
 
-def cold_cache_steps(step, n, dev):
-    """Secondary measurement: n more steps, each preceded (outside its event
-    pair) by a 512 MiB write that evicts the L2 caches and the 256 MB
-    Infinity Cache, so the step starts with its inputs in HBM only.  Returns
-    the per-step milliseconds."""
+FLUSH_BYTES = 512 << 20
+
+
+def timed_steps(step, steps, nev, flush=None):
+    """Run `steps` steps, step(events) recording `nev` HIP events on the
+    current stream; with `flush` (a device buffer), write it before each step,
+    outside the step's events.  Bracketed by torch.cuda.synchronize().
+    Returns (per-step event lists, wall seconds)."""
     import torch
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
-    for i in range(n):
-        flush.fill_(i & 0xFF)
-        evs[i][0].record()
-        step()
-        evs[i][1].record()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
     torch.cuda.synchronize()
-    del flush
-    return [e[0].elapsed_time(e[1]) for e in evs]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        step(evs[i])
+    torch.cuda.synchronize()
+    return evs, time.perf_counter() - t0
+
+
+def step_stats(ms):
+    """median (headline), p50, p95 and mean with its 95% Student-t half-width."""
+    s = sorted(ms)
+    n = len(s)
+    mean = statistics.mean(s)
+    sd = statistics.stdev(s) if n > 1 else 0.0
+    tcrit = {2: 12.706, 3: 4.303, 4: 3.182, 5: 2.776, 6: 2.571, 8: 2.365, 10: 2.262,
+             15: 2.145, 20: 2.093, 30: 2.045}.get(n, 1.96 if n > 30 else 2.1)
+    return {"median": statistics.median(s), "p50": s[n // 2],
+            "p95": s[min(n - 1, int(0.95 * n))], "mean": mean,
+            "ci95_half_width": tcrit * sd / math.sqrt(n) if n > 1 else None}
+
+
+def cpu_model():
+    """The host CPU's model name (lscpu's "Model name")."""
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for ln in out.splitlines():
+            if ln.strip().startswith("Model name"):
+                return ln.split(":", 1)[1].strip()
+    except Exception:  # pragma: no cover
+        pass
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return None
 
 
 def cpu_baseline(w, x, budget_s):
@@ -150,6 +193,7 @@ def cpu_baseline(w, x, budget_s):
         "kind": "oracle",
         "sample": f"{done} of {len(heads)} heads (fwd+bwd, fp64 NumPy, S and P materialised), "
                   f"{el:.1f} s",
+        "cpu_model": cpu_model(),
     }
 
 
@@ -225,22 +269,25 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # The secondary measurements first (K warm steps, then the two-stream
+    # steps), then the headline: K timed steps, each after a cache eviction.
+    # The GPU's clocks take a few tens of steps of sustained work to settle
+    # (a trace of five warm-up steps followed by the timed ones shows the
+    # dK/dV pass falling from ~375 to ~277 us over its first ~40 launches), so
+    # the headline comes last, at the clocks a training loop runs at.
     nev = len(phases) + 1
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    cold = cold_cache_steps(step, min(args.steps, 20), dev)
+    warm_evs, _ = timed_steps(step, args.steps, nev)
     two = two_stream_steps(args, step_parts=(q, k, v, o, lse, do, dq, dk, dv, sc, cz, mask, ws)) \
         if "dkdv" in phases else None
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    evs, wall = timed_steps(step, args.steps, nev, flush)
+    del flush
 
     per = {p: [e[i].elapsed_time(e[i + 1]) for e in evs] for i, p in enumerate(phases)}
     steps_ms = [e[0].elapsed_time(e[nev - 1]) for e in evs]
-    span_ms = evs[0][0].elapsed_time(evs[-1][nev - 1])
-    ms_step = span_ms / args.steps
+    warm_ms = [e[0].elapsed_time(e[nev - 1]) for e in warm_evs]
+    st = step_stats(steps_ms)
+    ms_step = st["median"]
     fl = accounting.flops(w.B, w.H, w.N, w.d, w.causal, x["mask"])
     elem = 2 if w.dtype == "bf16" else 4
     hb = accounting.hbm_bytes(w.B, w.H, w.N, w.d, elem)
@@ -249,6 +296,7 @@ def main():
     value = total / (ms_step * 1e-3) / 1e12
 
     avg = {p: statistics.mean(per[p]) for p in phases}
+    med = {p: statistics.median(per[p]) for p in phases}
     kflops = {"fwd": fl["fwd_kernel"], "dkdv": fl["dkdv_kernel"], "dq": fl["dq_kernel"],
               "bwd": fl["bwd"]}
     # The library runs bf16, d = 128 without a block mask on the ping-pong
@@ -269,26 +317,21 @@ def main():
         roof = {"kernel": names[dom], "bound": "mfma", "achieved": ach, "peak": peak,
                 "unit": "TFLOP/s", "frac": ach / peak,
                 "traffic": recorded_traffic(w.name, names[dom]),
-                "algorithmic_flops_per_launch": kflops[dom], "avg_launch_ms": avg[dom]}
+                "algorithmic_flops_per_launch": kflops[dom], "avg_launch_ms": avg[dom],
+                "launches_averaged": args.steps}
 
     kernels = {}
     for p in phases:
-        entry = {"avg_ms": avg[p], "median_ms": statistics.median(per[p])}
+        entry = {"avg_ms": avg[p], "median_ms": med[p]}
         if p in kflops:
             entry["tflops"] = kflops[p] / (avg[p] * 1e-3) / 1e12
         else:
             entry["gbs"] = hb["pre_kernel"] / (avg[p] * 1e-3) / 1e9
         kernels[names[p]] = entry
 
-    fwd_ms = avg["fwd"]
-    bwd_ms = avg["bwd"] if "bwd" in avg else avg["pre"] + avg["dkdv"] + avg["dq"]
-    s = sorted(steps_ms)
-    n = len(s)
-    mean = statistics.mean(s)
-    sd = statistics.stdev(s) if n > 1 else 0.0
-    # two-sided 95% Student t critical values for small samples, else normal
-    tcrit = {2: 12.706, 3: 4.303, 4: 3.182, 5: 2.776, 6: 2.571, 8: 2.365, 10: 2.262,
-             15: 2.145, 20: 2.093, 30: 2.045}.get(n, 1.96 if n > 30 else 2.1)
+    fwd_ms = med["fwd"]
+    bwd_ms = med["bwd"] if "bwd" in med else \
+        statistics.median([a + b + c for a, b, c in zip(per["pre"], per["dkdv"], per["dq"])])
 
     cpu = None
     if not args.no_cpu:
@@ -317,15 +360,18 @@ def main():
         "bwd_tflops": fl["bwd"] / (bwd_ms * 1e-3) / 1e12,
         "fwd_ms": fwd_ms,
         "bwd_ms": bwd_ms,
-        "step_ms_stats": {"mean": mean, "p50": s[n // 2], "p95": s[min(n - 1, int(0.95 * n))],
-                          "ci95_half_width": tcrit * sd / math.sqrt(n) if n > 1 else None},
+        "step_ms_stats": st,
+        "timing": f"median of {args.steps} steps, each after a {FLUSH_BYTES >> 20} MiB device "
+                  "write outside its HIP events (caches evicted); per-kernel HIP events on the "
+                  f"launch stream; order: {args.warmup} warm-up steps, {args.steps} warm steps "
+                  "(secondary), the two-stream steps (secondary), then these steps",
         "wall_s_timed": wall,
         "kernels": kernels,
         "roofline": roof,
         "cpu_baseline": cpu,
-        "cold_cache": {"ms_per_step_median": statistics.median(cold),
-                       "value": total / (statistics.median(cold) * 1e-3) / 1e12,
-                       "steps": len(cold), "flush_bytes": 512 << 20},
+        "warm": {"ms_per_step_median": statistics.median(warm_ms),
+                 "value": total / (statistics.median(warm_ms) * 1e-3) / 1e12,
+                 "steps": len(warm_ms)},
         "peak_tflops": peak,
     }
     if two is not None:
@@ -397,6 +443,7 @@ def cpu_baseline_decode(w, x, budget_s):
         "cores": int(threads),
         "kind": "oracle",
         "sample": f"{len(done)} of {w.B} sequences (all heads, fp64 NumPy), {el:.1f} s",
+        "cpu_model": cpu_model(),
     }
 
 
@@ -416,29 +463,28 @@ def bench_fp8(args, w):
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     copy_probe(args, dev)
 
-    def step():
+    def step(ev=None):
+        if ev: ev[0].record()
         fa.fa_fwd_fp8(t["q8"], t["k8"], t["vt8"], t["sq"], t["sk"], t["sv"], o, lse, w.scale,
                       w.causal)
+        if ev: ev[1].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        evs[i][0].record()
-        step()
-        evs[i][1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    warm_evs, _ = timed_steps(step, args.steps, 2)          # secondary first (clocks settle)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    evs, wall = timed_steps(step, args.steps, 2, flush)
+    del flush
     per = [e[0].elapsed_time(e[1]) for e in evs]
-    ms_step = evs[0][0].elapsed_time(evs[-1][1]) / args.steps
+    st = step_stats(per)
+    ms_step = st["median"]
     fl = accounting.flops(w.B, w.H, w.N, w.d, w.causal, None)
     peak = 5000.0                                   # dense FP8 MFMA, TFLOP/s
     value = fl["fwd"] / (ms_step * 1e-3) / 1e12
     avg = statistics.mean(per)
     ach = fl["fwd_kernel"] / (avg * 1e-3) / 1e12
-    s = sorted(per)
+    warm_ms = statistics.median([e[0].elapsed_time(e[1]) for e in warm_evs])
     out = {
         "metric": "attention FP8 (E4M3) forward TFLOP/s (1 MI355X) and % of FP8 MFMA peak",
         "value": value,
@@ -455,14 +501,17 @@ def bench_fp8(args, w):
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "parallelism": "none (1 GPU)"},
         "pct_of_peak": 100.0 * value / peak,
-        "step_ms_stats": {"mean": statistics.mean(s), "p50": s[len(s) // 2],
-                          "p95": s[min(len(s) - 1, int(0.95 * len(s)))]},
+        "step_ms_stats": st,
+        "timing": f"median of {args.steps} calls, each after a {FLUSH_BYTES >> 20} MiB device "
+                  "write outside its HIP events (caches evicted), after the warm secondary",
         "wall_s_timed": wall,
         "roofline": {"kernel": "fa_fwd_fp8_kernel", "bound": "mfma", "achieved": ach,
                      "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
                      "traffic": recorded_traffic(w.name, "fa_fwd_fp8_kernel"),
                      "algorithmic_flops_per_launch": fl["fwd_kernel"], "avg_launch_ms": avg},
         "cpu_baseline": None,
+        "warm": {"ms_per_step_median": warm_ms,
+                 "value": fl["fwd"] / (warm_ms * 1e-3) / 1e12},
     }
     print(json.dumps(out))
 
@@ -496,22 +545,22 @@ def bench_decode(args):
     ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
     copy_probe(args, dev)
 
-    def step():
+    def step(ev=None):
+        if ev: ev[0].record()
         fa.fa_decode(q, k, v, o, lse, w.scale, sl, w.causal, 0, ws)
+        if ev: ev[1].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        evs[i][0].record()
-        step()
-        evs[i][1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    warm_evs, _ = timed_steps(step, args.steps, 2)          # secondary first (clocks settle)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    evs, wall = timed_steps(step, args.steps, 2, flush)
+    del flush
     per = [e[0].elapsed_time(e[1]) for e in evs]
-    ms_step = evs[0][0].elapsed_time(evs[-1][1]) / args.steps
+    st = step_stats(per)
+    ms_step = st["median"]
+    warm_ms = statistics.median([e[0].elapsed_time(e[1]) for e in warm_evs])
     elem = 2 if w.dtype == "bf16" else 4
     by = accounting.decode_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.d, elem, x["seqlens"])
     value = by["total"] / (ms_step * 1e-3) / 1e9
@@ -523,7 +572,6 @@ def bench_decode(args):
             "traffic": decode_traffic(w.name, S),
             "algorithmic_bytes_per_launch": by["total"], "avg_launch_ms": avg}
     cpu = None if args.no_cpu else cpu_baseline_decode(w, x, args.cpu_seconds)
-    s = sorted(per)
     out = {
         "metric": "decode attention HBM GB/s (bf16, 1 MI355X) and % of 8 TB/s",
         "value": value,
@@ -543,11 +591,13 @@ def bench_decode(args):
                    "parallelism": "none (1 GPU)"},
         "pct_of_peak": 100.0 * value / HBM_PEAK_GBS,
         "tflops": by["flops"] / (ms_step * 1e-3) / 1e12,
-        "step_ms_stats": {"mean": statistics.mean(s), "p50": s[len(s) // 2],
-                          "p95": s[min(len(s) - 1, int(0.95 * len(s)))]},
+        "step_ms_stats": st,
+        "timing": f"median of {args.steps} calls, each after a {FLUSH_BYTES >> 20} MiB device "
+                  "write outside its HIP events (caches evicted), after the warm secondary",
         "wall_s_timed": wall,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "warm": {"ms_per_step_median": warm_ms, "value": by["total"] / (warm_ms * 1e-3) / 1e9},
     }
     print(json.dumps(out))
 

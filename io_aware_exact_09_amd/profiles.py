@@ -1,7 +1,7 @@
 """Turn rocprofv3 output into the short text summaries kept under profiles/.
 
     python -m io_aware_exact_09_amd.profiles stats <kernel_stats.csv> <out.md> "<command>" \
-        [<kernel_trace.csv> <warmup> <steps>]
+        [<kernel_trace.csv> <warmup> <steps> [<secondary steps before the headline>]]
     python -m io_aware_exact_09_amd.profiles traffic <fetch_dir> <write_dir> <workload> \
         <out.json> "<fetch command>" "<write command>"
     python -m io_aware_exact_09_amd.profiles counters <out.md> <workload> \
@@ -73,6 +73,8 @@ def short_name(kernel_name: str) -> str:
             return k
     if "neg_kernel" in kernel_name:
         return PROBE
+    if "FillFunctor" in kernel_name or "fill" in kernel_name.lower():
+        return "fill (cache eviction):" + kernel_name[:40]
     if "copy" in kernel_name.lower() or "elementwise" in kernel_name:
         return "copy:" + kernel_name[:60]
     return kernel_name[:60]
@@ -87,12 +89,14 @@ def _rows(path_or_dir: str, suffix: str):
 
 
 def stats_summary(stats_csv: str, command: str, trace_csv: str | None = None,
-                  warmup: int = 0, steps: int = 0) -> str:
+                  warmup: int = 0, steps: int = 0, skip: int = 0) -> str:
     """Per-kernel calls and durations from a --kernel-trace --stats run.
 
-    With the per-dispatch trace and the bench's warm-up / timed step counts
-    (one launch of each kernel per step), a last column averages only the
-    dispatches of the timed steps: the launches the bench's HIP events time.
+    With the per-dispatch trace and the bench's step counts (one launch of
+    each kernel per step), a last column averages only the dispatches of the
+    headline's timed steps, the launches the bench's HIP events time: the
+    `steps` launches that follow the first `warmup + skip` ones (warm-up
+    steps, then the bench's secondary steps).
     """
     timed = {}
     if trace_csv:
@@ -102,14 +106,17 @@ def stats_summary(stats_csv: str, command: str, trace_csv: str | None = None,
             per.setdefault(short_name(r["Kernel_Name"]), []).append(
                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
         for k, v in per.items():
-            if len(v) >= warmup + steps and steps > 0:
-                timed[k] = statistics.fmean(v[warmup:warmup + steps])
+            if len(v) >= warmup + skip + steps and steps > 0:
+                timed[k] = statistics.fmean(v[warmup + skip:warmup + skip + steps])
     lines = ["# rocprofv3 kernel-trace summary", "", f"Command: `{command}`", ""]
     head = "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |"
     if timed:
-        lines += [f"Last column: average over dispatches {warmup + 1}..{warmup + steps} of each "
-                  f"kernel, the {steps} timed steps after {warmup} warm-up steps (the bench's "
-                  "HIP-event window; later dispatches are its cold-cache steps).", ""]
+        a, b = warmup + skip + 1, warmup + skip + steps
+        lines += [f"Last column: average over dispatches {a}..{b} of each kernel: the {steps} "
+                  f"headline steps, after {warmup} warm-up steps and {skip} secondary steps (the "
+                  "launches the bench's HIP events average for its headline and roofline; each "
+                  "follows a cache-evicting device write, the fill kernel listed separately). "
+                  "The other columns count every dispatch.", ""]
         head += " timed steps average (us) |"
     lines += [head, "|" + "---|" * (head.count("|") - 1)]
     for r in _rows(stats_csv, "kernel_stats.csv"):
@@ -235,6 +242,8 @@ def counters_table(passes, workload: str) -> str:
 def main(argv):
     if argv[0] == "stats":
         extra = (argv[4], int(argv[5]), int(argv[6])) if len(argv) > 6 else ()
+        if len(argv) > 7:
+            extra += (int(argv[7]),)
         text = stats_summary(argv[1], argv[3], *extra)
         open(argv[2], "w").write(text)
         print(text)
