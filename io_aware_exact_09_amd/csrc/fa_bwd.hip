@@ -71,16 +71,30 @@ fa_bwd_delta_kernel(const T* __restrict__ O, const T* __restrict__ dO, float* __
 //      dV^T += dO_i^T P     (A = dO^T by transposing LDS reads, B = P registers)
 //      dK^T += Q_i^T dS     (A = Q^T by transposing LDS reads, B = dS registers)
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int D>
 struct DkdvCfg {
   static constexpr int BK = 128;                         // keys per work-group
-  static constexpr int BQ = sizeof(T) == 2 ? 64 : 32;   // query rows per compute tile
-  static constexpr int SQ = 2 * BQ;                      // query rows per staged tile
+  // query rows per compute tile: 64 for bf16 at d = 128 (the software-
+  // pipelined tile body); 32 for fp32 and for bf16 at d = 64, whose two
+  // waves per SIMD leave registers for a simpler body only
+  static constexpr int BQ = (sizeof(T) == 2 && D == 128) ? 64 : 32;
+  static constexpr int SQ = sizeof(T) == 2 ? 128 : 64;   // query rows per staged tile
+};
+
+// Waves per SIMD of the dK/dV pass: one at d = 128 (the tile needs ~436
+// registers); two for bf16 at d = 64 (about half of that), so that two
+// work-groups share a compute unit and one's prologue and epilogue overlap
+// the other's tiles.  The two-wave build keeps operands in VGPRs (no AGPR
+// pins, see to_agpr).
+template <typename T, int D>
+struct DkdvOcc {
+  static constexpr int waves = (sizeof(T) == 2 && D == 64) ? 2 : 1;
+  static constexpr bool pin_agpr = waves == 1;
 };
 
 template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP>
 __global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
+__attribute__((amdgpu_waves_per_eu(DkdvOcc<T, D>::waves, DkdvOcc<T, D>::waves)))
 fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                    const T* __restrict__ dO, const float* __restrict__ LSE,
                    const float* __restrict__ delta, T* __restrict__ dK, T* __restrict__ dV,
@@ -89,7 +103,7 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
                    float c, float scale, DropParams drp) {
   using E = Elem<T>;
   using frag = typename E::frag;
-  using Cfg = DkdvCfg<T>;
+  using Cfg = DkdvCfg<T, D>;
   constexpr int BK = Cfg::BK, BQ = Cfg::BQ, SQ = Cfg::SQ;
   constexpr int NQH = BQ / 32;            // 32-row query halves per tile
   constexpr int NT = D / 16, ND = D / 32;
@@ -129,8 +143,10 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
     const uint32_t off = (uint32_t)krow * RB + (16 * t + 8 * g) * sizeof(T);
     kf[t] = gload_frag<T>(rk, off);
     vf[t] = gload_frag<T>(rv, off);
-    to_agpr(kf[t]);
-    to_agpr(vf[t]);
+    if constexpr (DkdvOcc<T, D>::pin_agpr) {
+      to_agpr(kf[t]);
+      to_agpr(vf[t]);
+    }
   }
 
   // Staged tiles of SQ query rows, each run as two compute tiles of BQ rows
@@ -222,8 +238,10 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
 #pragma unroll
         for (int t = 0; t < SB; ++t) {
           frag a = aq[t], o = ao[t];
-          to_agpr(a);      // at the consumer: a pin right after the read
-          to_agpr(o);      // would make the read wait for its data there
+          if constexpr (DkdvOcc<T, D>::pin_agpr) {
+            to_agpr(a);    // at the consumer: a pin right after the read
+            to_agpr(o);    // would make the read wait for its data there
+          }
           sv = E::mma(a, kf[t0 + t], sv);
           dpv = E::mma(o, vf[t0 + t], dpv);
         }
@@ -334,8 +352,10 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
 #pragma unroll
         for (int b = 0; b < ND; ++b) {
           frag o = ot[b], q = qt[b];
-          to_agpr(o);
-          to_agpr(q);
+          if constexpr (DkdvOcc<T, D>::pin_agpr) {
+            to_agpr(o);
+            to_agpr(q);
+          }
           dvacc[b] = E::mma(o, pf, dvacc[b]);
           dkacc[b] = E::mma(q, df, dkacc[b]);
         }
@@ -845,7 +865,7 @@ static DropParams drop_params(const BwdArgs& a) {
 
 template <typename T, int D, bool CAUSAL, bool MASKED>
 static hipError_t launch_dkdv_t(const BwdArgs& a) {
-  const int nkb = (a.N + DkdvCfg<T>::BK - 1) / DkdvCfg<T>::BK;
+  const int nkb = (a.N + DkdvCfg<T, D>::BK - 1) / DkdvCfg<T, D>::BK;
   auto go = [&](auto kernel) {
     // one work-group row per (key/value head, split of its query heads)
     const int rows = a.BH / a.G * a.gsplit;

@@ -42,6 +42,9 @@ OCCUPANCY = {
     ("fa_bwd_dkdv_kernel", ("bf16", 128, False, False, False)): 1,
     ("fa_bwd_dq_kernel", ("bf16", 128, True, False, False)): 2,
     ("fa_bwd_dq_kernel", ("bf16", 128, False, False, False)): 2,
+    # d = 64: two waves per SIMD (two work-groups per compute unit)
+    ("fa_bwd_dkdv_kernel", ("bf16", 64, True, False, False)): 2,
+    ("fa_bwd_dkdv_kernel", ("bf16", 64, False, True, False)): 2,
 }
 
 LDS_BYTES = 160 * 1024
