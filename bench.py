@@ -3,8 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long]
 
 A step is one pass of the whole hot path over one batch: fa_fwd, then the
-three backward phases (D preprocess, dK/dV pass, dQ pass), on torch's current
-stream, inputs resident in HBM.  W untimed warm-up steps; then the secondary
+two kernels of fa_bwd (the dQ pass, which also forms the row term D, then the
+dK/dV pass) through its phase entry points fa_bwd_dq_and_d and fa_bwd_dkdv,
+on torch's current stream, inputs resident in HBM.  W untimed warm-up steps; then the secondary
 measurements (K steps without cache eviction, "warm", and the two-stream steps);
 then exactly K timed steps bracketed by torch.cuda.synchronize(), the headline.
 Before each of those (outside its HIP events) a 512 MiB device write evicts L2
@@ -28,9 +29,9 @@ for fp32 workloads).
 
 The cpu_baseline leg times the CPU fp64 oracle on a bounded sample of the same
 workload (whole heads, about 10-30 s) on this host's cores.  Secondary fields:
-warm (the steps without the eviction) and two_stream_step (the dK/dV and dQ
-passes on two streams through the phase entry points; the headline step is
-fa_bwd's single stream).
+warm (the steps without the eviction) and two_stream_step (the staged phases:
+the D preprocess, then the dK/dV and dQ passes on two streams; the headline
+step is fa_bwd's single stream).
 
 Decode workloads (--workload decode | decode_mix | decode_spec): a step is one
 fa_decode call over the whole batch (64 sequences, 8K cache, 32 query heads
@@ -236,11 +237,11 @@ def main():
     if grouped and drop > 0:
         print("--dropout is not offered for grouped key/value heads", file=sys.stderr)
         sys.exit(2)
-    phases = ["fwd", "bwd"] if (drop > 0 or grouped) else ["fwd", "pre", "dkdv", "dq"]
+    phases = ["fwd", "bwd"] if (drop > 0 or grouped) else ["fwd", "dq", "dkdv"]
 
     def step(ev=None):
         if grouped:
-            # fa_fwd_gqa, then fa_bwd_gqa (its three kernels in one entry point)
+            # fa_fwd_gqa, then fa_bwd_gqa (its kernels in one entry point)
             if ev: ev[0].record()
             fa.fa_fwd_gqa(q, k, v, o, lse, sc, cz, mask)
             if ev: ev[1].record()
@@ -248,7 +249,7 @@ def main():
             if ev: ev[2].record()
             return
         if drop > 0:
-            # the backward's three kernels run inside one entry point here
+            # the backward's kernels run inside one entry point here
             if ev: ev[0].record()
             fa.fa_fwd_dropout(q, k, v, o, lse, sc, drop, 1234, cz, mask)
             if ev: ev[1].record()
@@ -258,12 +259,10 @@ def main():
         if ev: ev[0].record()
         fa.fa_fwd(q, k, v, o, lse, sc, cz, mask)
         if ev: ev[1].record()
-        fa.fa_bwd_preprocess(o, do, ws)
+        fa.fa_bwd_dq_and_d(q, k, v, o, do, lse, dq, sc, cz, mask, ws)
         if ev: ev[2].record()
         fa.fa_bwd_dkdv(q, k, v, do, lse, dk, dv, sc, cz, mask, ws)
         if ev: ev[3].record()
-        fa.fa_bwd_dq(q, k, v, do, lse, dq, sc, cz, mask, ws)
-        if ev: ev[4].record()
 
     for _ in range(args.warmup):
         step()
@@ -289,8 +288,6 @@ def main():
     st = step_stats(steps_ms)
     ms_step = st["median"]
     fl = accounting.flops(w.B, w.H, w.N, w.d, w.causal, x["mask"])
-    elem = 2 if w.dtype == "bf16" else 4
-    hb = accounting.hbm_bytes(w.B, w.H, w.N, w.d, elem)
     peak = PEAK_TFLOPS[w.dtype]
     total = fl["fwd"] + fl["bwd"]
     value = total / (ms_step * 1e-3) / 1e12
@@ -303,35 +300,24 @@ def main():
     # forward kernel, everything else on the four-wave one.
     fwd_name = ("fa_fwd_pp_kernel" if w.dtype == "bf16" and w.d == 128 and w.mask_density is None
                 and drop == 0 else "fa_fwd_kernel")
-    names = {"fwd": fwd_name, "pre": "fa_bwd_delta_kernel", "dkdv": "fa_bwd_dkdv_kernel",
-             "dq": "fa_bwd_dq_kernel",
-             "bwd": ("fa_bwd_gqa" if grouped else "fa_bwd_dropout") + " (three kernels)"}
+    names = {"fwd": fwd_name, "dkdv": "fa_bwd_dkdv_kernel", "dq": "fa_bwd_dq_kernel",
+             "bwd": ("fa_bwd_gqa" if grouped else "fa_bwd_dropout") + " (all its kernels)"}
     dom = max(phases, key=lambda p: avg[p])
-    if dom == "pre":
-        ach = hb["pre_kernel"] / (avg[dom] * 1e-3) / 1e9
-        roof = {"kernel": names[dom], "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                "traffic": recorded_traffic(w.name, names[dom])}
-    else:
-        ach = kflops[dom] / (avg[dom] * 1e-3) / 1e12
-        roof = {"kernel": names[dom], "bound": "mfma", "achieved": ach, "peak": peak,
-                "unit": "TFLOP/s", "frac": ach / peak,
-                "traffic": recorded_traffic(w.name, names[dom]),
-                "algorithmic_flops_per_launch": kflops[dom], "avg_launch_ms": avg[dom],
-                "launches_averaged": args.steps}
+    ach = kflops[dom] / (avg[dom] * 1e-3) / 1e12
+    roof = {"kernel": names[dom], "bound": "mfma", "achieved": ach, "peak": peak,
+            "unit": "TFLOP/s", "frac": ach / peak,
+            "traffic": recorded_traffic(w.name, names[dom]),
+            "algorithmic_flops_per_launch": kflops[dom], "avg_launch_ms": avg[dom],
+            "launches_averaged": args.steps}
 
     kernels = {}
     for p in phases:
-        entry = {"avg_ms": avg[p], "median_ms": med[p]}
-        if p in kflops:
-            entry["tflops"] = kflops[p] / (avg[p] * 1e-3) / 1e12
-        else:
-            entry["gbs"] = hb["pre_kernel"] / (avg[p] * 1e-3) / 1e9
-        kernels[names[p]] = entry
+        kernels[names[p]] = {"avg_ms": avg[p], "median_ms": med[p],
+                             "tflops": kflops[p] / (avg[p] * 1e-3) / 1e12}
 
     fwd_ms = med["fwd"]
     bwd_ms = med["bwd"] if "bwd" in med else \
-        statistics.median([a + b + c for a, b, c in zip(per["pre"], per["dkdv"], per["dq"])])
+        statistics.median([a + b for a, b in zip(per["dq"], per["dkdv"])])
 
     cpu = None
     if not args.no_cpu:

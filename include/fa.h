@@ -130,9 +130,10 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  * the closed form of the chain rule through softmax:
  *   D_i = sum_k dO_ik O_ik,  dV = P^T dO,  dP = dO V^T,
  *   dS = P * (dP - D 1^T),   dQ = scale * dS K,  dK = scale * dS^T Q.
- * Three kernels run in order on `stream`: the D preprocess, a pass that is
- * parallel over key blocks and accumulates dK and dV on chip, and a pass that
- * is parallel over query blocks and accumulates dQ on chip (no atomics).
+ * Two kernels run in order on `stream`: a pass that is parallel over query
+ * blocks, forms D from the O and dO rows it holds (writing it to the
+ * workspace) and accumulates dQ on chip (no atomics), then a pass that is
+ * parallel over key blocks, reads D and accumulates dK and dV on chip.
  * Tiles dropped by causality or the block mask are skipped in both passes.
  *
  *   Q, K, V, O, dO  in : [B,H,N,d] dtype; O and LSE from fa_fwd with the
@@ -150,11 +151,13 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O,
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The three phases of fa_bwd, callable one by one (fa_bwd is exactly
- * fa_bwd_preprocess, then fa_bwd_dkdv, then fa_bwd_dq, on one stream).  The
- * dK/dV and dQ passes only read what the preprocess wrote, so a caller may
- * enqueue them on two streams that both wait for the preprocess.  Arguments
- * have the meaning, layout and checks given for fa_bwd.
+ * The phases of the backward, callable one by one: fa_bwd_preprocess, then
+ * fa_bwd_dkdv and fa_bwd_dq give results bit-identical to fa_bwd's (whose
+ * dQ pass, fa_bwd_dq_and_d below, forms D itself, adding the same products
+ * in the same order as fa_bwd_preprocess).  The dK/dV and dQ passes only
+ * read what the preprocess wrote, so a caller may enqueue them on two
+ * streams that both wait for the preprocess.  Arguments have the meaning,
+ * layout and checks given for fa_bwd.
  *
  * fa_bwd_preprocess: workspace[i] = D_i = sum_k dO_ik O_ik (fp32), the
  *   row term of dS = P * (dP - D 1^T).
@@ -175,6 +178,20 @@ fa_status fa_bwd_dq(const void* Q, const void* K, const void* V, const void* dO,
                     const float* LSE, void* dQ, int B, int H, int N, int d, float scale,
                     int causal, const unsigned char* block_mask, fa_dtype dtype,
                     const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_bwd_dq_and_d -- fa_bwd's own first kernel: the dQ pass of fa_bwd_dq
+ * that also forms D_i = sum_k dO_ik O_ik from the O and dO rows it holds
+ * (instead of reading it) and writes it to the workspace, bit-identical to
+ * what fa_bwd_preprocess writes.  fa_bwd is exactly fa_bwd_dq_and_d, then
+ * fa_bwd_dkdv, on one stream.  Arguments as for fa_bwd; the workspace
+ * (at least 4 * B * H * N bytes) is written, not read.
+ */
+fa_status fa_bwd_dq_and_d(const void* Q, const void* K, const void* V, const void* O,
+                          const void* dO, const float* LSE, void* dQ, int B, int H, int N,
+                          int d, float scale, int causal, const unsigned char* block_mask,
+                          fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /*
  * fa_bwd_static -- fa_bwd for callers that cannot allocate device memory
@@ -242,7 +259,7 @@ fa_status fa_bwd_dropout(const void* Q, const void* K, const void* V, const void
  * checks as for fa_fwd / fa_bwd (with H = Hq).  Hkv = Hq gives exactly
  * fa_fwd / fa_bwd.  When B * Hkv * ceil(N/128) is small (under 512 work-groups)
  * a group's query heads are divided among up to G work-groups that each write
- * an fp32 partial dK, dV into the workspace, and a fourth kernel adds the
+ * an fp32 partial dK, dV into the workspace, and a third kernel adds the
  * partials in a fixed order (still deterministic).
  *
  * fa_bwd_gqa_workspace_bytes: 4 * B * Hq * N bytes for D, plus, when the dK/dV

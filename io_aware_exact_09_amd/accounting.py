@@ -48,6 +48,7 @@ def hbm_bytes(B: int, H: int, N: int, d: int, elem: int) -> dict:
         "pre_kernel": 2 * t + r,                     # read O dO, write D
         "dkdv_kernel": 4 * t + 2 * r + 2 * t,        # read Q K V dO LSE D, write dK dV
         "dq_kernel": 4 * t + 2 * r + t,              # read Q K V dO LSE D, write dQ
+        "dq_and_d_kernel": 5 * t + 2 * r + t,        # read Q K V O dO LSE, write D dQ
     }
 
 

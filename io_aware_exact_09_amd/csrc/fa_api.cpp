@@ -269,6 +269,28 @@ FA_EXPORT fa_status fa_bwd_dq(const void* Q, const void* K, const void* V, const
   return fa::launch_bwd_dq(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+FA_EXPORT fa_status fa_bwd_dq_and_d(const void* Q, const void* K, const void* V, const void* O,
+                                    const void* dO, const float* LSE, void* dQ, int B, int H,
+                                    int N, int d, float scale, int causal,
+                                    const unsigned char* block_mask, fa_dtype dtype,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  FA_TRY(check_buffers({{Q, 0, 0}, {K, 0, 0}, {V, 0, 0}, {O, 0, 0}, {dO, 0, 0}, {LSE, 0, 0}},
+                       {{dQ, 0, 0}}));
+  const Shape s{B, H, N, d, dtype};
+  FA_TRY(check_shape(s, scale));
+  const uintptr_t tb = s.tensor_bytes(), lb = s.row_bytes();
+  const Buf ws{workspace, workspace_bytes, 16};
+  const Buf m{block_mask, block_mask ? s.mask_bytes() : 0, 1};
+  FA_TRY(check_layout(
+      {{Q, tb, 16}, {K, tb, 16}, {V, tb, 16}, {O, tb, 16}, {dO, tb, 16}, {LSE, lb, 4}, m},
+      {{dQ, tb, 16}}, &ws, true, lb));
+  fa::BwdArgs a = bwd_args(s, scale, causal, block_mask, stream);
+  a.q = Q; a.k = K; a.v = V; a.o = O; a.dout = dO; a.lse = LSE; a.dq = dQ;
+  a.delta = static_cast<float*>(workspace);
+  a.dq_forms_delta = true;
+  return fa::launch_bwd_dq(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 FA_EXPORT fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O,
                            const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
                            int B, int H, int N, int d, float scale, int causal,
@@ -364,9 +386,11 @@ fa_status bwd_impl(const void* Q, const void* K, const void* V, const void* O, c
   a.dq = dQ; a.dk = dK; a.dv = dV;
   a.delta = static_cast<float*>(workspace);
   a.drop = drop;
-  if (fa::launch_bwd_preprocess(a) != hipSuccess) return FA_ERR_LAUNCH;
-  if (fa::launch_bwd_dkdv(a) != hipSuccess) return FA_ERR_LAUNCH;
+  // The dQ pass forms D itself (bit-identical to the preprocess kernel's) and
+  // writes it for the dK/dV pass, so it runs first and no preprocess runs.
+  a.dq_forms_delta = true;
   if (fa::launch_bwd_dq(a) != hipSuccess) return FA_ERR_LAUNCH;
+  if (fa::launch_bwd_dkdv(a) != hipSuccess) return FA_ERR_LAUNCH;
   return FA_OK;
 }
 

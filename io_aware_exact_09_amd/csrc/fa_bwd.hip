@@ -34,6 +34,18 @@
 
 namespace fa {
 
+// The dot product of one 16-byte chunk of an O row with the same chunk of
+// its dO row: one fma chain from zero, in element order.  Both places that
+// form D (the preprocess kernel and the dQ pass) build on it and then add the
+// chunk results in the same pairwise tree, so they give bit-identical D.
+template <typename T, int CH>
+__device__ __forceinline__ float chunk_dot(const T* a, const T* b) {
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < CH; ++e) acc = fmaf(Elem<T>::to_f32(a[e]), Elem<T>::to_f32(b[e]), acc);
+  return acc;
+}
+
 // ---------------------------------------------------------------------------
 // 1. D_i = sum_k dO_ik O_ik  (HBM-bound; one 16-byte chunk per lane)
 // ---------------------------------------------------------------------------
@@ -52,10 +64,7 @@ fa_bwd_delta_kernel(const T* __restrict__ O, const T* __restrict__ dO, float* __
   if (row < rows) {
     const u32x4 a = *reinterpret_cast<const u32x4*>(O + (size_t)row * D + col);
     const u32x4 b = *reinterpret_cast<const u32x4*>(dO + (size_t)row * D + col);
-    const T* pa = reinterpret_cast<const T*>(&a);
-    const T* pb = reinterpret_cast<const T*>(&b);
-#pragma unroll
-    for (int e = 0; e < CH; ++e) acc = fmaf(E::to_f32(pa[e]), E::to_f32(pb[e]), acc);
+    acc = chunk_dot<T, CH>(reinterpret_cast<const T*>(&a), reinterpret_cast<const T*>(&b));
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
@@ -583,7 +592,51 @@ fa_bwd_dkdv_reduce_kernel(const float* __restrict__ part, T* __restrict__ dK,
 //      dP^T = V_j dO_i^T    (A = V rows from LDS, B = dO registers)
 //      P^T, dS^T elementwise with this lane's own LSE_i and D_i
 //      dQ^T += K_j^T dS^T   (A = K^T via transposing LDS reads, B = dS^T)
+//    D_i comes from the preprocess kernel, or (given O) the pass forms it
+//    from the O and dO rows in its registers and writes it for the dK/dV
+//    pass, which then runs after it.
 // ---------------------------------------------------------------------------
+// D_i for the row that lane pair (l32, l32 + 32) holds in the dQ layout:
+// lane (l32, g) has the 8-element operand chunk at column 16t + 8g of O (o)
+// and dO (d), t = 0..D/16-1, i.e. 16-byte chunks 2t + g (bf16) or 4t + 2g
+// and 4t + 2g + 1 (fp32).  The chunk results are added in the preprocess
+// kernel's tree (partners at chunk-index distance LPR/2, ..., 2, 1): strides
+// inside a lane's own chunks add in registers, the stride between g = 0 and
+// g = 1 takes one cross-lane swap.  Both lanes of the pair return D_i.
+template <typename T, int D>
+__device__ __forceinline__ float pair_row_delta(const typename Elem<T>::frag* o,
+                                                const typename Elem<T>::frag* d) {
+  constexpr int CH = Elem<T>::kPerChunk, LPR = D / CH, NJ = LPR / 2, NT = D / 16;
+  constexpr int GSTRIDE = sizeof(T) == 2 ? 1 : 2;   // chunk-index distance between g = 0, 1
+  float a[NJ];                                      // a[j]: this lane's j-th chunk
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if constexpr (sizeof(T) == 2) {
+      a[t] = chunk_dot<T, CH>(reinterpret_cast<const T*>(&o[t].v),
+                              reinterpret_cast<const T*>(&d[t].v));
+    } else {
+      a[2 * t] = chunk_dot<T, CH>(reinterpret_cast<const T*>(&o[t].lo),
+                                  reinterpret_cast<const T*>(&d[t].lo));
+      a[2 * t + 1] = chunk_dot<T, CH>(reinterpret_cast<const T*>(&o[t].hi),
+                                      reinterpret_cast<const T*>(&d[t].hi));
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) {
+    if (off == GSTRIDE) {
+      // Chunks still live here: j < GSTRIDE (wider strides already folded).
+#pragma unroll
+      for (int j = 0; j < GSTRIDE; ++j) a[j] += __shfl_xor(a[j], 32);
+    } else {
+      const int jo = off > GSTRIDE ? off / 2 : off;   // the same distance in j
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        if (!(j & jo)) a[j] += a[j ^ jo];
+    }
+  }
+  return a[0];
+}
+
 template <typename T>
 struct DqCfg {
   static constexpr int BR = 128;
@@ -594,8 +647,8 @@ template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(Occupancy<T, D>::dq, Occupancy<T, D>::dq)))
 fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-                 const T* __restrict__ dO, const float* __restrict__ LSE,
-                 const float* __restrict__ delta, T* __restrict__ dQ,
+                 const T* __restrict__ dO, const T* __restrict__ O, const float* __restrict__ LSE,
+                 float* __restrict__ delta, T* __restrict__ dQ,
                  const uint8_t* __restrict__ mask, int BH, int kv_group, int N, int T_tiles,
                  float c, float scale, DropParams drp) {
   using E = Elem<T>;
@@ -632,7 +685,19 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   }
   // Rows past N, and rows that keep no key (LSE = -inf), get P = 0.
   const float lrow = buf_load_f32(make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4), (uint32_t)qrow * 4);
-  const float dval = buf_load_f32(make_rsrc(delta + (size_t)bh * N, (uint32_t)N * 4), (uint32_t)qrow * 4);
+  // D_i: formed here from O (when given, which the pass then writes for the
+  // dK/dV pass), else read from what the preprocess kernel wrote.
+  const rsrc_t rd = make_rsrc(delta + (size_t)bh * N, (uint32_t)N * 4);
+  frag oo[NT];
+  float dval = 0.f;
+  if (O) {
+    const rsrc_t rO = make_rsrc(O + head, (uint32_t)N * RB);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      oo[t] = gload_frag<T>(rO, (uint32_t)qrow * RB + (16 * t + 8 * g) * sizeof(T));
+  } else {
+    dval = buf_load_f32(rd, (uint32_t)qrow * 4);
+  }
 
   const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
   const int ntiles = (kv_end + BC - 1) / BC;
@@ -663,6 +728,10 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   if (j < ntiles) stage(j, IntTag<0>{});
   wait_global_loads();
   const float lse2 = (qrow < N && lrow != neg_inf()) ? lrow * kLog2e : pos_inf();
+  if (O) {
+    dval = pair_row_delta<T, D>(oo, of);
+    if (g == 0 && qrow < N) delta[(size_t)bh * N + qrow] = dval;
+  }
 
   // One key tile.  MASKED_TILE: the tile crosses this wave's causal diagonal
   // or the end of the sequence (a compile-time tag where a second body fits
@@ -892,7 +961,8 @@ static hipError_t launch_dq_t(const BwdArgs& a) {
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3(nqb * a.BH), dim3(kThreads), 0, a.stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                       static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
+                       static_cast<const T*>(a.v), static_cast<const T*>(a.dout),
+                       a.dq_forms_delta ? static_cast<const T*>(a.o) : nullptr, a.lse, a.delta,
                        static_cast<T*>(a.dq), a.mask, a.BH, a.G, a.N, a.T, score_coef(a.scale),
                        a.scale, drop_params(a));
   };

@@ -35,6 +35,7 @@ struct BwdArgs {
   const float* lse;
   void* dq; void* dk; void* dv;
   float* delta;            // workspace: D_i = rowsum(dO * O), [BH * N] fp32
+  bool dq_forms_delta = false;  // the dQ pass forms D from O and writes delta
   const uint8_t* mask;
   int BH, N, d, T;         // BH = B * (query heads)
   int G = 1;               // query heads per key/value head (K, V, dK, dV have BH / G heads)

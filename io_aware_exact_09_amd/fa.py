@@ -74,6 +74,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa_bwd_dkdv.restype = i
         lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp]
         lib.fa_bwd_dq.restype = i
+        lib.fa_bwd_dq_and_d.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i,
+                                        vp, sz, vp]
+        lib.fa_bwd_dq_and_d.restype = i
         u64 = ctypes.c_ulonglong
         lib.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, f, u64, i, vp]
         lib.fa_fwd_dropout.restype = i
@@ -294,6 +297,21 @@ def fa_bwd_dq(q, k, v, do, lse, dq, scale, causal=False, block_mask=None, worksp
                        float(scale), int(bool(causal)), _ptr(block_mask), _dtype_code(q),
                        _ptr(workspace), _nbytes(workspace), _stream(stream))
     _check(st, "fa_bwd_dq")
+
+
+def fa_bwd_dq_and_d(q, k, v, o, do, lse, dq, scale, causal=False, block_mask=None,
+                    workspace=None, stream=None) -> None:
+    """dQ pass that forms D from O and dO and writes it to ``workspace``
+    (fa_bwd is this, then fa_bwd_dkdv)."""
+    lib = load_library()
+    _check_tensors(q, dict(q=q, k=k, v=v, o=o, do=do, lse=lse, dq=dq, workspace=workspace))
+    _mask_ok(q, block_mask)
+    B, H, N, d = q.shape
+    st = lib.fa_bwd_dq_and_d(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                             B, H, N, d, float(scale), int(bool(causal)), _ptr(block_mask),
+                             _dtype_code(q), _ptr(workspace), _nbytes(workspace),
+                             _stream(stream))
+    _check(st, "fa_bwd_dq_and_d")
 
 
 def fa_bwd_gqa_workspace_bytes(B: int, Hq: int, Hkv: int, N: int, d: int) -> int:

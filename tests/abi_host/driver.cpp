@@ -22,6 +22,7 @@ extern int g_launches;
 extern int g_scratch_lookups;
 extern FwdArgs g_fwd;
 extern BwdArgs g_bwd;
+extern BwdArgs g_dq;   // the last dQ-pass launch
 extern Fp8FwdArgs g_fp8;
 extern DecodeArgs g_dec;
 }  // namespace fa
@@ -115,15 +116,16 @@ static void forward_cases() {
 static void backward_cases() {
   const size_t need = fa_bwd_workspace_bytes(2, 16, 4096, 128);
   EXPECT(need == 4ull * 2 * 16 * 4096);
-  ACCEPT(3, bwd(2, 16, 4096, 128, 0.1f, FA_BF16, P(9), need));
+  ACCEPT(2, bwd(2, 16, 4096, 128, 0.1f, FA_BF16, P(9), need));
   EXPECT(fa::g_bwd.delta == F(9) && fa::g_bwd.gsplit == 1 && fa::g_bwd.part == nullptr);
-  ACCEPT(3, bwd(2, 16, 4096, 128, -0.1f, FA_BF16, P(9), need));
+  EXPECT(fa::g_dq.dq_forms_delta && fa::g_dq.o == P(3) && fa::g_dq.delta == F(9));
+  ACCEPT(2, bwd(2, 16, 4096, 128, -0.1f, FA_BF16, P(9), need));
   REJECT(FA_ERR_WORKSPACE, bwd(2, 16, 4096, 128, 0.1f, FA_BF16, P(9), need - 1));
   REJECT(FA_ERR_WORKSPACE, bwd(2, 16, 4096, 128, 0.1f, FA_BF16, nullptr, need));
   REJECT(FA_ERR_WORKSPACE, bwd(2, 16, 4096, 128, 0.1f, FA_BF16, P(9, 4), need));
   REJECT(FA_ERR_ALIAS, bwd(2, 16, 4096, 128, 0.1f, FA_BF16, P(5), need));   // over LSE
   REJECT(FA_ERR_ALIGN, bwd(1, 1, 128, 64, 0.1f, FA_BF16, P(9), 4096, P(7, 8)));
-  ACCEPT(3, bwd(1, 1, 8388352, 128, 0.1f, FA_FP32, P(9), 4ull * 8388352));
+  ACCEPT(2, bwd(1, 1, 8388352, 128, 0.1f, FA_FP32, P(9), 4ull * 8388352));
   REJECT(FA_ERR_SHAPE, bwd(1, 1, 8388353, 128, 0.1f, FA_FP32, P(9), 1ull << 30));
   EXPECT(fa_bwd_workspace_bytes(0, 1, 1, 64) == 0);
   EXPECT(fa_bwd_workspace_bytes(1, 1, 1, 96) == 0);
@@ -132,14 +134,14 @@ static void backward_cases() {
   // grouped heads: 256 work-groups are split in two, partials after D
   const size_t gneed = fa_bwd_gqa_workspace_bytes(2, 16, 4, 4096, 128);
   EXPECT(gneed == 4ull * 2 * 16 * 4096 + 2ull * 2 * 2 * 4 * 4096 * 128 * 4);
-  ACCEPT(3, fa_bwd_gqa(P(0), P(1), P(2), P(3), P(4), F(5), P(6), P(7), P(8), 2, 16, 4, 4096, 128,
+  ACCEPT(2, fa_bwd_gqa(P(0), P(1), P(2), P(3), P(4), F(5), P(6), P(7), P(8), 2, 16, 4, 4096, 128,
                        0.1f, 1, nullptr, FA_BF16, P(9), gneed, nullptr));
   EXPECT(fa::g_bwd.gsplit == 2 && fa::g_bwd.G == 4);
   EXPECT((char*)fa::g_bwd.part == (char*)P(9) + 4 * 2 * 16 * 4096);
   REJECT(FA_ERR_WORKSPACE, fa_bwd_gqa(P(0), P(1), P(2), P(3), P(4), F(5), P(6), P(7), P(8), 2,
                                       16, 4, 4096, 128, 0.1f, 1, nullptr, FA_BF16, P(9),
                                       gneed - 16, nullptr));
-  ACCEPT(3, fa_bwd_dropout(P(0), P(1), P(2), P(3), P(4), F(5), P(6), P(7), P(8), 1, 2, 300, 64,
+  ACCEPT(2, fa_bwd_dropout(P(0), P(1), P(2), P(3), P(4), F(5), P(6), P(7), P(8), 1, 2, 300, 64,
                            0.1f, 1, nullptr, 0.5f, 7, FA_BF16, P(9), 4096, nullptr));
   EXPECT(fa::g_bwd.drop.on && fa::g_bwd.drop.inv_keep == 2.0f);
   // the phases one by one
@@ -152,16 +154,24 @@ static void backward_cases() {
                                    0.1f, 1, nullptr, FA_BF16, P(9), need, nullptr));
   ACCEPT(1, fa_bwd_dq(P(0), P(1), P(2), P(4), F(5), P(6), 2, 16, 4096, 128, 0.1f, 1, M(10),
                       FA_BF16, P(9), need, nullptr));
+  EXPECT(!fa::g_dq.dq_forms_delta);
+  ACCEPT(1, fa_bwd_dq_and_d(P(0), P(1), P(2), P(3), P(4), F(5), P(6), 2, 16, 4096, 128, 0.1f,
+                            1, nullptr, FA_BF16, P(9), need, nullptr));
+  EXPECT(fa::g_dq.dq_forms_delta && fa::g_dq.o == P(3) && fa::g_dq.delta == F(9));
+  REJECT(FA_ERR_ALIAS, fa_bwd_dq_and_d(P(0), P(1), P(2), P(3), P(4), F(5), P(6), 2, 16, 4096,
+                                       128, 0.1f, 1, nullptr, FA_BF16, P(3, 64), need, nullptr));
+  REJECT(FA_ERR_NULL, fa_bwd_dq_and_d(P(0), P(1), P(2), nullptr, P(4), F(5), P(6), 2, 16, 4096,
+                                      128, 0.1f, 1, nullptr, FA_BF16, P(9), need, nullptr));
   REJECT(FA_ERR_DTYPE, fa_bwd_dq(P(0), P(1), P(2), P(4), F(5), P(6), 2, 16, 4096, 128, 0.1f, 1,
                                  nullptr, (fa_dtype)3, P(9), need, nullptr));
 }
 
 static void static_scratch_cases() {
   const int rows = FA_STATIC_SCRATCH_BYTES / 4;
-  ACCEPT(3, fa_bwd_static(P(0), P(1), P(2), P(3), P(4), F(5), P(6), P(7), P(8), 2, 16, 4096,
+  ACCEPT(2, fa_bwd_static(P(0), P(1), P(2), P(3), P(4), F(5), P(6), P(7), P(8), 2, 16, 4096,
                           128, 0.1f, 1, nullptr, FA_BF16, nullptr));
   EXPECT((uintptr_t)fa::g_bwd.delta == 0x7e0000000000ull && fa::g_bwd.gsplit == 1);
-  ACCEPT(3, fa_bwd_static(P(0), P(1), P(2), P(3), P(4), F(5), P(6), P(7), P(8), 1, 1, rows, 64,
+  ACCEPT(2, fa_bwd_static(P(0), P(1), P(2), P(3), P(4), F(5), P(6), P(7), P(8), 1, 1, rows, 64,
                           -0.1f, 0, nullptr, FA_FP32, nullptr));
   const int looked = fa::g_scratch_lookups;
   REJECT(FA_ERR_SCRATCH, fa_bwd_static(P(0), P(1), P(2), P(3), P(4), F(5), P(6), P(7), P(8), 1,

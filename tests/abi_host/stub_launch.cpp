@@ -10,6 +10,7 @@ namespace fa {
 int g_launches = 0;
 FwdArgs g_fwd;
 BwdArgs g_bwd;
+BwdArgs g_dq;
 Fp8FwdArgs g_fp8;
 DecodeArgs g_dec;
 
@@ -17,7 +18,9 @@ hipError_t launch_fwd(const FwdArgs& a) { ++g_launches; g_fwd = a; return hipSuc
 hipError_t launch_fwd_fp8(const Fp8FwdArgs& a) { ++g_launches; g_fp8 = a; return hipSuccess; }
 hipError_t launch_bwd_preprocess(const BwdArgs& a) { ++g_launches; g_bwd = a; return hipSuccess; }
 hipError_t launch_bwd_dkdv(const BwdArgs& a) { ++g_launches; g_bwd = a; return hipSuccess; }
-hipError_t launch_bwd_dq(const BwdArgs& a) { ++g_launches; g_bwd = a; return hipSuccess; }
+hipError_t launch_bwd_dq(const BwdArgs& a) {
+  ++g_launches; g_bwd = a; g_dq = a; return hipSuccess;
+}
 hipError_t launch_decode(const DecodeArgs& a) { ++g_launches; g_dec = a; return hipSuccess; }
 
 // The static scratch's device address: a fixed fake address here.

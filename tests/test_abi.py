@@ -34,7 +34,7 @@ def test_header_symbols_are_exported(lib):
                           "fa_fwd_dropout", "fa_bwd_dropout", "fa_decode", "fa_fwd_gqa",
                           "fa_bwd_gqa", "fa_fwd_fp8", "fa_bwd_gqa_workspace_bytes",
                           "fa_decode_num_splits", "fa_decode_workspace_bytes",
-                          "fa_bwd_static"}
+                          "fa_bwd_static", "fa_bwd_dq_and_d"}
     out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -259,6 +259,18 @@ def test_phase_validation(lib):
     assert lib.fa_bwd_dq(*bad) == 6
     bad = list(args); bad[13] = 3
     assert lib.fa_bwd_dq(*bad) == 4
+    # dq_and_d: (Q, K, V, O, dO, LSE, dQ, B, H, N, d, scale, causal, mask, dtype, ws, wsb,
+    # stream); it writes the workspace, so the workspace may overlap no input
+    args = [p(0), p(1), p(2), p(3), p(4), p(5), p(6), 1, 2, 128, 64, 0.125, 1, None, BF16, p(7),
+            1 << 20, None]
+    bad = list(args); bad[3] = None
+    assert lib.fa_bwd_dq_and_d(*bad) == 1
+    bad = list(args); bad[15] = p(3, 64)       # workspace over O
+    assert lib.fa_bwd_dq_and_d(*bad) == 9
+    bad = list(args); bad[16] = 1023
+    assert lib.fa_bwd_dq_and_d(*bad) == 6
+    bad = list(args); bad[10] = 96
+    assert lib.fa_bwd_dq_and_d(*bad) == 3
 
 
 def test_single_hip_runtime_in_process(lib):
