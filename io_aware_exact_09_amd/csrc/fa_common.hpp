@@ -92,6 +92,17 @@ __device__ __forceinline__ unsigned char* pick(int v, unsigned char* b0, unsigne
 }
 template <int V> __device__ __forceinline__ constexpr IntTag<V ^ 1> other(IntTag<V>) { return {}; }
 __device__ __forceinline__ int other(int v) { return v ^ 1; }
+// The same for a ring of three arrays.
+template <int V>
+__device__ __forceinline__ unsigned char* pick3(IntTag<V>, unsigned char* a, unsigned char* b,
+                                                unsigned char* c) {
+  return V == 0 ? a : (V == 1 ? b : c);
+}
+template <int V>
+__device__ __forceinline__ unsigned char* pick4(IntTag<V>, unsigned char* a, unsigned char* b,
+                                                unsigned char* c, unsigned char* d) {
+  return V == 0 ? a : (V == 1 ? b : (V == 2 ? c : d));
+}
 
 // Philox4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel random
 // numbers: as easy as 1, 2, 3", SC 2011), written from the paper's

@@ -58,12 +58,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | 0x0F70 | (N & 15));
 }
 
-template <int V>
-__device__ __forceinline__ unsigned char* pick4(IntTag<V>, unsigned char* a, unsigned char* b,
-                                                unsigned char* c, unsigned char* d) {
-  return V == 0 ? a : (V == 1 ? b : (V == 2 ? c : d));
-}
-
 template <typename T, int D, bool CAUSAL, int WAVES, int NBUF>
 __global__ void __launch_bounds__(64 * WAVES)
 fa_decode_split_kernel(const T* __restrict__ Q, const T* __restrict__ K,

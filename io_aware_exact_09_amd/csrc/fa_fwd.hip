@@ -322,12 +322,6 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
 // tile s+1 is first read.  The loop is unrolled by three steps so the slots
 // are compile-time choices of three distinct arrays (see pick()).
 // ---------------------------------------------------------------------------
-template <int V>
-__device__ __forceinline__ unsigned char* pick3(IntTag<V>, unsigned char* a, unsigned char* b,
-                                                unsigned char* c) {
-  return V == 0 ? a : (V == 1 ? b : c);
-}
-
 template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(2 * kThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2)))

@@ -78,6 +78,8 @@ SMALL = [
     (2, 1, 1024, 128, False, None),
     (1, 2, 16, 128, True, None),
     (1, 2, 528, 128, False, "rand"),
+    (1, 2, 304, 64, True, None),
+    (1, 1, 720, 64, False, None),
 ]
 
 
