@@ -11,7 +11,8 @@ then exactly K timed steps bracketed by torch.cuda.synchronize(), the headline.
 Before each of those (outside its HIP events) a 512 MiB device write evicts L2
 and the 256 MB Infinity Cache, so every timed step starts with its inputs in
 HBM only; each kernel of the step is bracketed by HIP events on the same
-stream.  The headline is the median step time of those K steps, taken last
+stream, created without the system-scope fence (HipEvent), so that recording
+them does not flush the caches between the kernels.  The headline is the median step time of those K steps, taken last
 because the GPU's clocks need a few tens of steps of sustained work to settle.
 Prints ONE JSON line.
 
@@ -114,13 +115,70 @@ def copy_probe(args, dev):
 FLUSH_BYTES = 512 << 20
 
 
+class HipEvent:
+    """A HIP timing event on torch's current stream, created with
+    hipEventDisableSystemFence.  Recording a default event ends with a
+    system-scope release, which writes back and invalidates the GPU caches
+    and so slows the kernel launched after it (measured: a step with events
+    between its kernels ran up to 8% longer on the 1K-token workload); this
+    event only takes the timestamp.  The timed steps end with
+    torch.cuda.synchronize(), which orders the host's reads of the times."""
+
+    _hip = None
+    FLAGS = 0x20000000       # hipEventDisableSystemFence
+
+    @classmethod
+    def runtime(cls):
+        # The HIP runtime torch has already mapped (one copy per process).
+        if cls._hip is None:
+            import ctypes
+            maps = open("/proc/self/maps").read()
+            paths = sorted({ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln})
+            if not paths:
+                raise RuntimeError("no HIP runtime mapped (import torch and touch the GPU first)")
+            hip = ctypes.CDLL(paths[0])
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = hip
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._ct = ctypes
+        self.h = ctypes.c_void_p()
+        st = self.runtime().hipEventCreateWithFlags(ctypes.byref(self.h), self.FLAGS)
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
+
+    def record(self):
+        import torch
+        st = self._hip.hipEventRecord(self.h, self._ct.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord failed ({st})")
+
+    def elapsed_time(self, end) -> float:
+        """Milliseconds from this event to `end` (both recorded and complete)."""
+        ms = self._ct.c_float()
+        st = self._hip.hipEventElapsedTime(self._ct.byref(ms), self.h, end.h)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st})")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.h:
+            self._hip.hipEventDestroy(self.h)
+
+
 def timed_steps(step, steps, nev, flush=None):
     """Run `steps` steps, step(events) recording `nev` HIP events on the
     current stream; with `flush` (a device buffer), write it before each step,
     outside the step's events.  Bracketed by torch.cuda.synchronize().
     Returns (per-step event lists, wall seconds)."""
     import torch
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
+    evs = [[HipEvent() for _ in range(nev)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
@@ -348,8 +406,9 @@ def main():
         "bwd_ms": bwd_ms,
         "step_ms_stats": st,
         "timing": f"median of {args.steps} steps, each after a {FLUSH_BYTES >> 20} MiB device "
-                  "write outside its HIP events (caches evicted); per-kernel HIP events on the "
-                  f"launch stream; order: {args.warmup} warm-up steps, {args.steps} warm steps "
+                  "write outside its HIP events (caches evicted); per-kernel HIP events "
+                  f"(no system-scope fence) on the launch stream; order: {args.warmup} warm-up "
+                  f"steps, {args.steps} warm steps "
                   "(secondary), the two-stream steps (secondary), then these steps",
         "wall_s_timed": wall,
         "kernels": kernels,
@@ -388,7 +447,7 @@ def two_stream_steps(args, step_parts):
 
     for _ in range(5):
         step2()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = HipEvent(), HipEvent()
     torch.cuda.synchronize()
     e0.record()
     for _ in range(args.steps):
