@@ -5,15 +5,19 @@
 A step is one pass of the whole hot path over one batch: fa_fwd, then the
 two kernels of fa_bwd (the dQ pass, which also forms the row term D, then the
 dK/dV pass) through its phase entry points fa_bwd_dq_and_d and fa_bwd_dkdv,
-on torch's current stream, inputs resident in HBM.  W untimed warm-up steps; then the secondary
-measurements (K steps without cache eviction, "warm", and the two-stream steps);
-then exactly K timed steps bracketed by torch.cuda.synchronize(), the headline.
-Before each of those (outside its HIP events) a 512 MiB device write evicts L2
-and the 256 MB Infinity Cache, so every timed step starts with its inputs in
-HBM only; each kernel of the step is bracketed by HIP events on the same
-stream, created without the system-scope fence (HipEvent), so that recording
-them does not flush the caches between the kernels.  The headline is the median step time of those K steps, taken last
-because the GPU's clocks need a few tens of steps of sustained work to settle.
+on torch's current stream, inputs resident in HBM.  W untimed warm-up steps;
+then the secondary measurements (K steps without cache eviction, "warm", and
+the two-stream steps); then exactly K timed steps bracketed by
+torch.cuda.synchronize(), the headline.  Before each of those (outside its
+HIP events) a read of a 512 MiB device buffer evicts L2 and the 256 MB
+Infinity Cache, so every timed step starts with its inputs in HBM only.  The
+eviction reads rather than writes: a write would leave hundreds of MB of
+dirty lines in the caches, whose write-back the timed step would then pay
+for.  Each kernel of the step is bracketed by HIP events on the same stream,
+created without the system-scope fence (HipEvent), so that recording them
+does not flush the caches between the kernels.  The headline is the median
+step time of those K steps, taken last because the GPU's clocks need a few
+tens of steps of sustained work to settle.
 Prints ONE JSON line.
 
 Workloads are seeded synthetic inputs with the shapes of the FlashAttention
@@ -172,10 +176,25 @@ class HipEvent:
             self._hip.hipEventDestroy(self.h)
 
 
+def eviction_buffer(dev):
+    """FLUSH_BYTES of device memory, written once and settled, whose read
+    (evict()) replaces the contents of L2 and the Infinity Cache."""
+    import torch
+    buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+    evict(buf)
+    torch.cuda.synchronize()
+    return buf
+
+
+def evict(buf):
+    """Read the whole eviction buffer (a reduction kernel; leaves clean lines)."""
+    return buf.sum()
+
+
 def timed_steps(step, steps, nev, flush=None):
     """Run `steps` steps, step(events) recording `nev` HIP events on the
-    current stream; with `flush` (a device buffer), write it before each step,
-    outside the step's events.  Bracketed by torch.cuda.synchronize().
+    current stream; with `flush` (an eviction_buffer), read it before each
+    step, outside the step's events.  Bracketed by torch.cuda.synchronize().
     Returns (per-step event lists, wall seconds)."""
     import torch
     evs = [[HipEvent() for _ in range(nev)] for _ in range(steps)]
@@ -183,7 +202,7 @@ def timed_steps(step, steps, nev, flush=None):
     t0 = time.perf_counter()
     for i in range(steps):
         if flush is not None:
-            flush.fill_(i & 0xFF)
+            evict(flush)
         step(evs[i])
     torch.cuda.synchronize()
     return evs, time.perf_counter() - t0
@@ -336,7 +355,7 @@ def main():
     warm_evs, _ = timed_steps(step, args.steps, nev)
     two = two_stream_steps(args, step_parts=(q, k, v, o, lse, do, dq, dk, dv, sc, cz, mask, ws)) \
         if "dkdv" in phases else None
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush = eviction_buffer(dev)
     evs, wall = timed_steps(step, args.steps, nev, flush)
     del flush
 
@@ -405,8 +424,8 @@ def main():
         "fwd_ms": fwd_ms,
         "bwd_ms": bwd_ms,
         "step_ms_stats": st,
-        "timing": f"median of {args.steps} steps, each after a {FLUSH_BYTES >> 20} MiB device "
-                  "write outside its HIP events (caches evicted); per-kernel HIP events "
+        "timing": f"median of {args.steps} steps, each after a read of a {FLUSH_BYTES >> 20} MiB "
+                  "device buffer outside its HIP events (caches evicted); per-kernel HIP events "
                   f"(no system-scope fence) on the launch stream; order: {args.warmup} warm-up "
                   f"steps, {args.steps} warm steps "
                   "(secondary), the two-stream steps (secondary), then these steps",
@@ -518,7 +537,7 @@ def bench_fp8(args, w):
         step()
     torch.cuda.synchronize()
     warm_evs, _ = timed_steps(step, args.steps, 2)          # secondary first (clocks settle)
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush = eviction_buffer(dev)
     evs, wall = timed_steps(step, args.steps, 2, flush)
     del flush
     per = [e[0].elapsed_time(e[1]) for e in evs]
@@ -547,8 +566,9 @@ def bench_fp8(args, w):
                    "causal": w.causal, "parallelism": "none (1 GPU)"},
         "pct_of_peak": 100.0 * value / peak,
         "step_ms_stats": st,
-        "timing": f"median of {args.steps} calls, each after a {FLUSH_BYTES >> 20} MiB device "
-                  "write outside its HIP events (caches evicted), after the warm secondary",
+        "timing": f"median of {args.steps} calls, each after a read of a {FLUSH_BYTES >> 20} MiB "
+                  "device buffer outside its HIP events (caches evicted), after the warm "
+                  "secondary",
         "wall_s_timed": wall,
         "roofline": {"kernel": "fa_fwd_fp8_kernel", "bound": "mfma", "achieved": ach,
                      "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
@@ -599,7 +619,7 @@ def bench_decode(args):
         step()
     torch.cuda.synchronize()
     warm_evs, _ = timed_steps(step, args.steps, 2)          # secondary first (clocks settle)
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush = eviction_buffer(dev)
     evs, wall = timed_steps(step, args.steps, 2, flush)
     del flush
     per = [e[0].elapsed_time(e[1]) for e in evs]
@@ -637,8 +657,9 @@ def bench_decode(args):
         "pct_of_peak": 100.0 * value / HBM_PEAK_GBS,
         "tflops": by["flops"] / (ms_step * 1e-3) / 1e12,
         "step_ms_stats": st,
-        "timing": f"median of {args.steps} calls, each after a {FLUSH_BYTES >> 20} MiB device "
-                  "write outside its HIP events (caches evicted), after the warm secondary",
+        "timing": f"median of {args.steps} calls, each after a read of a {FLUSH_BYTES >> 20} MiB "
+                  "device buffer outside its HIP events (caches evicted), after the warm "
+                  "secondary",
         "wall_s_timed": wall,
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -73,8 +73,10 @@ def short_name(kernel_name: str) -> str:
             return k
     if "neg_kernel" in kernel_name:
         return PROBE
+    if "reduce_kernel" in kernel_name:
+        return "reduction (cache eviction):" + kernel_name[:40]
     if "FillFunctor" in kernel_name or "fill" in kernel_name.lower():
-        return "fill (cache eviction):" + kernel_name[:40]
+        return "fill:" + kernel_name[:40]
     if "copy" in kernel_name.lower() or "elementwise" in kernel_name:
         return "copy:" + kernel_name[:60]
     return kernel_name[:60]
@@ -115,7 +117,8 @@ def stats_summary(stats_csv: str, command: str, trace_csv: str | None = None,
         lines += [f"Last column: average over dispatches {a}..{b} of each kernel: the {steps} "
                   f"headline steps, after {warmup} warm-up steps and {skip} secondary steps (the "
                   "launches the bench's HIP events average for its headline and roofline; each "
-                  "follows a cache-evicting device write, the fill kernel listed separately). "
+                  "follows a cache-evicting read of a device buffer, the reduction kernel listed "
+                  "separately). "
                   "The other columns count every dispatch.", ""]
         head += " timed steps average (us) |"
     lines += [head, "|" + "---|" * (head.count("|") - 1)]
