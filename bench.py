@@ -82,6 +82,10 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain device copy of FA_COPY_PROBE_BYTES (512 MiB) first, "
                          "to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--no-two-stream", action="store_true",
+                    help="skip the two-stream secondary (its staged phases launch the D "
+                         "preprocess and a dQ pass that reads D; counter runs leave it out so "
+                         "that every dQ launch is the headline's)")
     return ap.parse_args()
 
 
@@ -354,7 +358,7 @@ def main():
     nev = len(phases) + 1
     warm_evs, _ = timed_steps(step, args.steps, nev)
     two = two_stream_steps(args, step_parts=(q, k, v, o, lse, do, dq, dk, dv, sc, cz, mask, ws)) \
-        if "dkdv" in phases else None
+        if "dkdv" in phases and not args.no_two_stream else None
     flush = eviction_buffer(dev)
     evs, wall = timed_steps(step, args.steps, nev, flush)
     del flush
