@@ -184,14 +184,16 @@ def eviction_buffer(dev):
     """FLUSH_BYTES of device memory, written once and settled, whose read
     (evict()) replaces the contents of L2 and the Infinity Cache."""
     import torch
-    buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+    buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     evict(buf)
     torch.cuda.synchronize()
     return buf
 
 
 def evict(buf):
-    """Read the whole eviction buffer (a reduction kernel; leaves clean lines)."""
+    """Read the whole eviction buffer: one fp32 reduction kernel, which leaves
+    clean lines (an int32 sum would first widen the buffer to int64 in a
+    temporary, writing 1 GiB)."""
     return buf.sum()
 
 
