@@ -732,6 +732,16 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
     dval = pair_row_delta<T, D>(oo, of);
     if (g == 0 && qrow < N) delta[(size_t)bh * N + qrow] = dval;
   }
+  // Starting value of every dP accumulator: -D (times 1 - p under dropout),
+  // so the matrix cores return dP - D and the tile needs no subtraction.
+  // Under dropout a kept entry is (dP - D (1-p)) / (1-p) = dP M - D; at
+  // p = 0 both paths do the same operations.
+  f32x16 dinit;
+  {
+    const float d0 = DROP ? -dval * (1.0f / drp.inv_keep) : -dval;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dinit[r] = d0;
+  }
 
   // One key tile.  MASKED_TILE: the tile crosses this wave's causal diagonal
   // or the end of the sequence (a compile-time tag where a second body fits
@@ -745,7 +755,7 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
       // Operands in sub-batches of SB chunks (register budget of two waves
       // per SIMD); the other wave on the SIMD covers the LDS latency.
       constexpr int SB = NT >= 8 ? 4 : NT;
-      f32x16 s = f32x16{}, dp = f32x16{};
+      f32x16 s = f32x16{}, dp = dinit;
 #pragma unroll
       for (int t0 = 0; t0 < NT; t0 += SB) {
         frag ak[SB], av[SB];
@@ -780,14 +790,14 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
           for (int x = 0; x < 4; ++x) {
             const int r = 4 * a + x;
             const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
-            dp[r] = p * (z.w[x] >= drp.thresh ? fmaf(dp[r], drp.inv_keep, -dval) : -dval);
+            dp[r] = p * (z.w[x] >= drp.thresh ? dp[r] * drp.inv_keep : -dval);
           }
         }
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
-          dp[r] = p * (dp[r] - dval);
+          dp[r] = p * dp[r];
         }
       }
       // Keys this row does not keep get dS = 0 (a select, so an overflowed P
