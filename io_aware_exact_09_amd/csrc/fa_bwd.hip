@@ -294,8 +294,23 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
         for (int a = a0; a < a1; ++a) {
           const int qi = 32 * qh + 8 * a + 4 * g;
           lv[a - a0] = *reinterpret_cast<const f32x4*>(sLt + qi);
-          dv[a - a0] = *reinterpret_cast<const f32x4*>(sDt + qi);
+          if constexpr (DROP) dv[a - a0] = *reinterpret_cast<const f32x4*>(sDt + qi);
         }
+      };
+      // LDS reads per register group in stat_load (LSE, and D for dropout)
+      constexpr int NSTAT = DROP ? 2 : 1;
+      // The dP accumulators of query half qh start at the LDS D row values,
+      // -D (times 1 - p under dropout; see step), so the matrix cores return
+      // dP - D and pds_part needs no subtraction.
+      auto dinit = [&](int qh) {
+        f32x16 v;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(sDt + 32 * qh + 8 * a + 4 * g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[4 * a + e] = x[e];
+        }
+        return v;
       };
       // P = 2^(S c - LSE log2 e), dS = P (dP - D) for register groups
       // a0 .. a1-1 (register r holds query 32qh + 8(r/4) + 4g + r%4), with the
@@ -309,7 +324,8 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
         for (int a = a0; a < a1; ++a) {
           const int qi = 32 * qh + 8 * a + 4 * g;
           const f32x4 lv = LOOK ? lvs[a - a0] : *reinterpret_cast<const f32x4*>(sLt + qi);
-          const f32x4 dv = LOOK ? dvs[a - a0] : *reinterpret_cast<const f32x4*>(sDt + qi);
+          f32x4 dv = f32x4{};
+          if constexpr (DROP) dv = LOOK ? dvs[a - a0] : *reinterpret_cast<const f32x4*>(sDt + qi);
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
             const int r = 4 * a + x;
@@ -320,10 +336,12 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
               // the end); dS = P (dP M - D) with M = Z / (1-p).
               const bool keep = (kbits[qh] >> r) & 1u;
               sv[r] = keep ? p : 0.f;
-              dpv[r] = p * (keep ? fmaf(dpv[r], drp.inv_keep, -dv[x]) : -dv[x]);
+              // dpv = dP - D (1-p): kept, (dP - D (1-p)) / (1-p) = dP M - D;
+              // dropped, -D = (-D (1-p)) / (1-p) from the LDS row value.
+              dpv[r] = p * (keep ? dpv[r] : dv[x]) * drp.inv_keep;
             } else {
               sv[r] = p;
-              dpv[r] = p * (dpv[r] - dv[x]);
+              dpv[r] = p * dpv[r];
             }
           }
         }
@@ -370,7 +388,7 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
         }
       };
 
-      f32x16 s0 = f32x16{}, dp0 = f32x16{};
+      f32x16 s0 = f32x16{}, dp0 = dinit(0);
       frag pf0[2], df0[2];
       frag xa[SB], xb[SB];        // operand set of the block being issued
       frag ya[SB], yb[SB];        // operand set prefetched for the next block
@@ -392,8 +410,10 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
           if (k + 1 < NSB) sdp_read(0, (k + 1) * SB, ya, yb);
           else sdp_read(1, 0, ya, yb);
           if (LOOK && k + 1 == NSB) stat_load(0, 0, GP, lc, dc);
+          if (k + 1 == NSB) dp1 = dinit(1);
           sdp_mma(k * SB, xa, xb, s0, dp0);
-          if (LOOK && k + 1 == NSB) interleave<2 * SB, 2 * SB + 2 * GP, 0>();
+          if (LOOK && k + 1 == NSB) interleave<2 * SB, 2 * SB + NSTAT * GP + 4, 0>();
+          else if (k + 1 == NSB) interleave<2 * SB, 2 * SB + 4, 0>();
           else interleave<2 * SB, 2 * SB, 0>();
           sched_fence();
 #pragma unroll
@@ -411,8 +431,8 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
           sdp_mma(k * SB, xa, xb, s1, dp1);
           pds_part(0, k * GP, (k + 1) * GP, s0, dp0, lc, dc);
           if (k + 1 == NSB) pds_pack(s0, dp0, pf0, df0);
-          if (k + 1 < NSB) interleave<2 * SB, 2 * SB + 2 * GP, 5>();
-          else interleave<2 * SB, 4 * ND + (LOOK ? 4 : 2 * GP), 5>();
+          if (k + 1 < NSB) interleave<2 * SB, 2 * SB + NSTAT * GP, 5>();
+          else interleave<2 * SB, 4 * ND + (LOOK ? 2 * NSTAT : NSTAT * GP), 5>();
           sched_fence();
 #pragma unroll
           for (int t = 0; t < SB; ++t) { xa[t] = ya[t]; xb[t] = yb[t]; }
@@ -423,14 +443,14 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
         if constexpr (LOOK) stat_load(1, 2, 4, ln, dn);
         dvdk_mma(ta, tb, pf0[0], df0[0]);
         pds_part(1, 0, 2, s1, dp1, lc, dc);
-        interleave<2 * ND, 4 * ND + 4, 6>();
+        interleave<2 * ND, 4 * ND + 2 * NSTAT, 6>();
         sched_fence();
         if constexpr (LOOK) stat_next();
         dvdk_read(1, 0, ta, tb);
         dvdk_mma(ua, ub, pf0[1], df0[1]);
         pds_part(1, 2, 4, s1, dp1, lc, dc);
         pds_pack(s1, dp1, pf1, df1);
-        interleave<2 * ND, 4 * ND + (LOOK ? 0 : 4), 6>();
+        interleave<2 * ND, 4 * ND + (LOOK ? 0 : 2 * NSTAT), 6>();
         sched_fence();
         // dV/dK, half 1
         dvdk_read(1, 1, ua, ub);
@@ -465,7 +485,9 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
     if (tid < SQ) {
       // Rows past N, and rows that keep no key (LSE = -inf), get P = 0.
       sL[BUF][tid] = (lrow_pre < N && lpre != neg_inf()) ? lpre * kLog2e : pos_inf();
-      sD[BUF][tid] = dpre;
+      // -D, the dP accumulators' starting value (see dinit); under dropout
+      // -D (1-p), exactly -D at p = 0.
+      sD[BUF][tid] = DROP ? -dpre * (1.0f / drp.inv_keep) : -dpre;
     }
     __syncthreads();
     if (un < NU) stage(un, other(buf_sel));
