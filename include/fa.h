@@ -224,10 +224,14 @@ fa_status fa_bwd_static(const void* Q, const void* K, const void* V, const void*
  *   dV = (P * M)^T dO,  dP = (dO V^T) * M,  D_i = sum_k dO_ik O_ik,
  *   dS = P * (dP - D 1^T),  dQ = scale * dS K,  dK = scale * dS^T Q.
  * Z is never stored: both calls regenerate it.  Element (i, j) (query i,
- * key j) of head bh = b*H + h is kept iff word (j mod 4) of Philox4x32 with
- * 10 rounds (Salmon, Moraes, Dror, Shaw, SC 2011) on counter
- * (j / 4, i, bh, 0) with key (seed mod 2^32, seed / 2^32) is
- * >= floor(dropout_p * 2^32).  fa_bwd_dropout must get the dropout_p and
+ * key j) of head bh = b*H + h takes word (j mod 4) of Philox4x32 with 10
+ * rounds (Salmon, Moraes, Dror, Shaw, SC 2011) on counter (j / 4, i / 2, bh, 0)
+ * with key (seed mod 2^32, seed / 2^32) -- its low 16 bits for even i, its
+ * high 16 bits for odd i -- and is kept iff that value is
+ * >= min(floor(dropout_p * 2^16), 2^16 - 1) (one call covers two queries and
+ * four keys; the drop rate is within 2^-16 of dropout_p, the kept
+ * probabilities are scaled by 1 / (1 - dropout_p)).  fa_bwd_dropout must get
+ * the dropout_p and
  * seed that fa_fwd_dropout got (and its O and LSE).  Other arguments as for
  * fa_fwd / fa_bwd; dropout_p must lie in [0, 1) (else FA_ERR_ARG).
  */

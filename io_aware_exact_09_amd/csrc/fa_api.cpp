@@ -110,11 +110,11 @@ fa::BwdArgs bwd_args(const Shape& s, float scale, int causal, const unsigned cha
 // Dropout probability p in [0, 1) and seed -> kernel parameters.
 fa_status dropout_params(float p, unsigned long long seed, fa::Dropout* out) {
   if (!std::isfinite(p) || p < 0.f || p >= 1.f) return FA_ERR_ARG;
-  const double t = std::floor((double)p * 4294967296.0);
+  const double t = std::floor((double)p * 65536.0);
   out->on = true;
   out->key0 = (uint32_t)(seed & 0xFFFFFFFFull);
   out->key1 = (uint32_t)(seed >> 32);
-  out->thresh = t >= 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
+  out->thresh = t >= 65535.0 ? 0xFFFFu : (uint32_t)t;
   out->inv_keep = (float)(1.0 / (1.0 - (double)p));
   return FA_OK;
 }

@@ -257,21 +257,25 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
       };
       // Dropout keep bits of query half qh: bit r for register r (query
       // 32qh + 8(r/4) + 4g + r%4, key krow).  A Philox call yields the words of
-      // four consecutive keys, i.e. of the four lanes of a lane quad, so lane
-      // m of the quad draws the calls of registers 4m..4m+3 for the whole quad
-      // and the quad exchanges the 16 keep bits each lane drew (DPP
-      // broadcasts): 4 calls per lane instead of 16.
+      // four consecutive keys, i.e. of the four lanes of a lane quad, for a
+      // query pair (low 16 bits for the even query, high for the odd one), so
+      // lane m of the quad draws the two calls of registers 4m..4m+3 for the
+      // whole quad and the quad exchanges the 16 keep bits each lane drew (DPP
+      // broadcasts): 2 calls per lane instead of 16.
       uint32_t kbits[NQH];
       auto drop_bits = [&](int qh) -> uint32_t {
         const int m = l32 & 3;
-        uint32_t mine = 0;      // bit 4x + k: call of register 4m + x, key of quad lane k
+        uint32_t mine = 0;      // bit 4x + k: register 4m + x, key of quad lane k
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
+        for (int y = 0; y < 2; ++y) {   // registers 4m + 2y (low halves), 4m + 2y + 1 (high)
           const Philox4 z = philox4x32_10((uint32_t)krow >> 2,
-                                          (uint32_t)(q0 + 32 * qh + 8 * m + 4 * g + x),
+                                          (uint32_t)(q0 + 32 * qh + 8 * m + 4 * g + 2 * y) >> 1,
                                           (uint32_t)bhq, 0u, drp.key0, drp.key1);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) mine |= (uint32_t)(z.w[k] >= drp.thresh) << (4 * x + k);
+          for (int k = 0; k < 4; ++k) {
+            mine |= (uint32_t)((z.w[k] & 0xFFFFu) >= drp.thresh) << (8 * y + k);
+            mine |= (uint32_t)((z.w[k] >> 16) >= drp.thresh) << (8 * y + 4 + k);
+          }
         }
         // this lane's bits (k = m) of quad lane src's draws -> registers 4src..4src+3
         auto mine_of = [&](auto src_tag) {
@@ -695,6 +699,11 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   const T* Kh = K + kvhead;
   const T* Vh = V + kvhead;
   const int qrow = q0 + 32 * w + l32;
+  // Dropout: the low 16-bit half of a Philox word for an even query row,
+  // the high half for an odd one.
+  const int odd = l32 & 1;
+  const uint32_t hmask = odd ? 0xFFFFFFFFu : 0xFFFFu;
+  const uint32_t hthr = odd ? drp.thresh << 16 : drp.thresh;
 
   const rsrc_t rq = make_rsrc(Q + head, (uint32_t)N * RB);
   const rsrc_t ro = make_rsrc(dO + head, (uint32_t)N * RB);
@@ -803,17 +812,25 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
       const int lim = (CAUSAL ? min(N, qrow + 1) : N) - kv0 - 4 * g - 32 * h;
       if constexpr (DROP) {
         // dS = P (dP M - D), M = Z / (1-p); registers 4a..4a+3 are keys
-        // kv0 + 32h + 8a + 4g + x, one Philox call per group of four.
+        // kv0 + 32h + 8a + 4g + x.  As in the forward, lanes l32 and l32 ^ 1
+        // (a query pair) share the Philox calls: the even lane draws groups
+        // a = 0, 1, the odd lane a = 2, 3, each reads the other's words over
+        // DPP and keeps its own 16-bit half.
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const Philox4 z = philox4x32_10((uint32_t)((kv0 + 32 * h + 8 * a) >> 2) + g,
-                                          (uint32_t)qrow, (uint32_t)bh, 0u, drp.key0, drp.key1);
+        for (int c2 = 0; c2 < 2; ++c2) {   // groups c2 (even lane's call), 2 + c2 (odd lane's)
+          const Philox4 z = philox4x32_10((uint32_t)((kv0 + 32 * h + 8 * (2 * odd + c2)) >> 2) + g,
+                                          (uint32_t)qrow >> 1, (uint32_t)bh, 0u, drp.key0, drp.key1);
 #pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const int r = 4 * a + x;
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
-            dp[r] = p * (z.w[x] >= drp.thresh ? dp[r] * drp.inv_keep : -dval);
-          }
+          for (int e = 0; e < 2; ++e)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              const int r = 4 * (2 * e + c2) + x;
+              const uint32_t wv = (uint32_t)(e == 0
+                  ? __builtin_amdgcn_mov_dpp((int)z.w[x], 0xA0, 0xF, 0xF, true)
+                  : __builtin_amdgcn_mov_dpp((int)z.w[x], 0xF5, 0xF, 0xF, true));
+              const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
+              dp[r] = p * ((wv & hmask) >= hthr ? dp[r] * drp.inv_keep : -dval);
+            }
         }
       } else {
 #pragma unroll

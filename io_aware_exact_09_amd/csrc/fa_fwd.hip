@@ -70,6 +70,12 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   const T* Kh = K + kvhead;
   const T* Vh = V + kvhead;
   const int qrow = q0 + 32 * w + l32;
+  // Dropout: this lane's 16-bit half of a Philox word is the low one for an
+  // even query row (w & 0xFFFF >= T), the high one for an odd row
+  // (w >= T << 16).
+  const int odd = l32 & 1;
+  const uint32_t hmask = odd ? 0xFFFFFFFFu : 0xFFFFu;
+  const uint32_t hthr = odd ? dp.thresh << 16 : dp.thresh;
 
   // Query fragments (B operand, natural order): Q[qrow][16t + 8g .. +7];
   // rows past N read as zero.
@@ -194,17 +200,25 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     // ---- dropout: zero the dropped probabilities (the row sum above keeps
     // them: softmax statistics are those of the undropped P; the 1/(1-p) of
     // the kept ones is applied to O at the end).  Registers 4a..4a+3 of half h
-    // are keys kv0 + 32h + 8a + 4g + x, one Philox call per group of four.
+    // are keys kv0 + 32h + 8a + 4g + x.  A Philox call covers four keys of a
+    // query pair (2y, 2y + 1), i.e. of lanes l32 and l32 ^ 1: the even lane
+    // draws the calls of groups a = 0, 1, the odd lane those of a = 2, 3, and
+    // both read each group's words from the lane that drew them (DPP quad
+    // broadcasts), each keeping its own 16-bit half.
     if constexpr (DROP) {
 #pragma unroll
       for (int h = 0; h < NH; ++h)
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const Philox4 z = philox4x32_10((uint32_t)((kv0 + 32 * h + 8 * a) >> 2) + g,
-                                          (uint32_t)qrow, (uint32_t)bh, 0u, dp.key0, dp.key1);
+        for (int c2 = 0; c2 < 2; ++c2) {   // groups c2 (even lane's call), 2 + c2 (odd lane's)
+          const Philox4 z = philox4x32_10((uint32_t)((kv0 + 32 * h + 8 * (2 * odd + c2)) >> 2) + g,
+                                          (uint32_t)qrow >> 1, (uint32_t)bh, 0u, dp.key0, dp.key1);
 #pragma unroll
-          for (int x = 0; x < 4; ++x)
-            if (z.w[x] < dp.thresh) s[h][4 * a + x] = 0.f;
+          for (int x = 0; x < 4; ++x) {
+            const uint32_t we = (uint32_t)__builtin_amdgcn_mov_dpp((int)z.w[x], 0xA0, 0xF, 0xF, true);
+            const uint32_t wo = (uint32_t)__builtin_amdgcn_mov_dpp((int)z.w[x], 0xF5, 0xF, 0xF, true);
+            if ((we & hmask) < hthr) s[h][4 * c2 + x] = 0.f;
+            if ((wo & hmask) < hthr) s[h][4 * (2 + c2) + x] = 0.f;
+          }
         }
     }
 

@@ -8,9 +8,10 @@
 namespace fa {
 
 // Dropout on the attention probabilities (see philox4x32_10 in
-// fa_common.hpp): element (i, j) of head bh is kept iff word j % 4 of
-// Philox4x32-10(counter (j / 4, i, bh, 0), key (key0, key1)) >= thresh;
-// kept probabilities are scaled by inv_keep = 1 / (1 - p).
+// fa_common.hpp): element (i, j) of head bh is kept iff the 16-bit half
+// i % 2 (0 low, 1 high) of word j % 4 of Philox4x32-10(counter
+// (j / 4, i / 2, bh, 0), key (key0, key1)) is >= thresh (< 2^16); kept
+// probabilities are scaled by inv_keep = 1 / (1 - p).
 struct Dropout {
   bool on = false;
   uint32_t key0 = 0, key1 = 0;

@@ -20,11 +20,15 @@ the rest of the pages support):
         dS = P * (dP - D 1^T),  dQ = scale dS K,  dK = scale dS^T Q.
   * The mask is not stored: forward and backward regenerate it from a
     counter-based generator, Philox4x32 with 10 rounds (Salmon, Moraes, Dror,
-    Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011).  Element
-    (i, j) of head bh (= b H + h) takes word j mod 4 of
-        Philox4x32-10(counter = (j // 4, i, bh, 0), key = (seed mod 2^32,
-                      seed // 2^32))
-    and is kept iff that word is >= T = floor(p 2^32) (so p = 0 keeps all).
+    Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011).  One call
+    serves a 2 x 4 block of the score matrix: element (i, j) of head bh
+    (= b H + h) takes word j mod 4 of
+        Philox4x32-10(counter = (j // 4, i // 2, bh, 0), key = (seed mod 2^32,
+                      seed // 2^32)),
+    its low 16 bits for even i and its high 16 bits for odd i, and is kept
+    iff that 16-bit value is >= T = floor(p 2^16) (clamped to 2^16 - 1; p = 0
+    keeps all).  The drop probability is so T / 2^16, within 2^-16 of p; the
+    kept probabilities are still scaled by 1 / (1 - p).
 
 The generator is written from its published definition below, in numpy
 uint64 arithmetic; nothing is shared with the GPU library.
@@ -70,23 +74,28 @@ def philox4x32(ctr, key, rounds: int = 10):
     return tuple(x.astype(np.uint32) for x in (c0, c1, c2, c3))
 
 
+MASK16 = 0xFFFF
+
+
 def threshold(p: float) -> int:
-    """Integer keep threshold T = floor(p 2^32) (clamped to 2^32 - 1)."""
+    """Integer keep threshold T = floor(p 2^16) (clamped to 2^16 - 1)."""
     if not (0.0 <= p < 1.0):
         raise ValueError("dropout probability must lie in [0, 1)")
-    return min(int(np.floor(p * 4294967296.0)), MASK32)
+    return min(int(np.floor(p * 65536.0)), MASK16)
 
 
 def keep_mask(bh: int, rows, cols, p: float, seed: int) -> np.ndarray:
     """Boolean keep mask Z[rows, cols] of head bh (see the module docstring)."""
     rows = np.asarray(rows, dtype=np.uint64)[:, None]
     cols = np.asarray(cols, dtype=np.uint64)[None, :]
-    words = philox4x32((cols >> np.uint64(2), rows, np.full_like(cols, bh), np.zeros_like(cols)),
+    words = philox4x32((cols >> np.uint64(2), rows >> np.uint64(1), np.full_like(cols, bh),
+                        np.zeros_like(cols)),
                        (seed & MASK32, (seed >> 32) & MASK32))
     w = np.stack(np.broadcast_arrays(*words), axis=-1)          # [rows, cols, 4]
     pick = (cols & np.uint64(3)).astype(np.int64)
     r = np.take_along_axis(w, np.broadcast_to(pick, w.shape[:2])[..., None], axis=-1)[..., 0]
-    return r >= np.uint32(threshold(p))
+    half = (r.astype(np.uint64) >> (np.uint64(16) * (rows & np.uint64(1)))) & np.uint64(MASK16)
+    return half >= np.uint64(threshold(p))
 
 
 def forward_backward(q, k, v, do, scale: float, p: float, seed: int, causal: bool = False,

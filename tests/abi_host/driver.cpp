@@ -102,7 +102,10 @@ static void forward_cases() {
   ACCEPT(1, fa_fwd_dropout(P(0), P(1), P(2), P(3), F(4), 1, 2, 300, 64, 0.1f, 1, nullptr, 0.25f,
                            0x123456789abcull, FA_BF16, nullptr));
   EXPECT(fa::g_fwd.drop.on && fa::g_fwd.drop.key0 == 0x56789abcu && fa::g_fwd.drop.key1 == 0x1234u);
-  EXPECT(fa::g_fwd.drop.thresh == 1073741824u);
+  EXPECT(fa::g_fwd.drop.thresh == 16384u);   // floor(0.25 * 2^16)
+  ACCEPT(1, fa_fwd_dropout(P(0), P(1), P(2), P(3), F(4), 1, 2, 300, 64, 0.1f, 1, nullptr,
+                           0.99999f, 1, FA_BF16, nullptr));
+  EXPECT(fa::g_fwd.drop.thresh == 65535u);   // clamped below 2^16
   for (float p : {-0.1f, 1.0f, NAN, INFINITY})
     REJECT(FA_ERR_ARG, fa_fwd_dropout(P(0), P(1), P(2), P(3), F(4), 1, 2, 300, 64, 0.1f, 1,
                                       nullptr, p, 1, FA_BF16, nullptr));

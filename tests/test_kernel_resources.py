@@ -23,15 +23,12 @@ SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_fwd_fp8.hip"]
 # Kernels are named by (function, template arguments) with bf16 as "bf16",
 # float as "f32", integers and bools as Python values.
 #
-# Known to spill: the dQ pass with dropout, bf16, d = 128, without the causal
-# mask (block mask on or off).  Next to the tile's operands, the Philox state
-# and keep bits leave no room in the 256 registers of two waves per SIMD for
-# a second tile body; with one body (the mask under a wave-uniform branch)
-# 5-13 VGPRs still spill, against ~105 with two.  The causal and d = 64
-# dropout kernels fit.
+# Known to spill: the dK/dV pass with dropout and a block mask, bf16,
+# d = 128, without the causal mask.  At one wave per SIMD it uses all 512
+# registers (256 VGPRs, 256 AGPRs); 4 VGPRs more go to spill slots in the
+# accumulation registers (no scratch memory).  The other dropout kernels fit.
 SCRATCH_ALLOWED = {
-    ("fa_bwd_dq_kernel", ("bf16", 128, False, False, True)),
-    ("fa_bwd_dq_kernel", ("bf16", 128, False, True, True)),
+    ("fa_bwd_dkdv_kernel", ("bf16", 128, False, True, True)),
 }
 
 # Waves per SIMD the kernels are laid out for (bf16, d = 128, no dropout).

@@ -40,7 +40,9 @@ def test_philox_round_count_matters():
 
 def test_threshold_and_keep_fraction():
     assert od.threshold(0.0) == 0
-    assert od.threshold(0.5) == 2 ** 31
+    assert od.threshold(0.5) == 2 ** 15
+    assert od.threshold(0.1) == 6553                    # floor(0.1 * 65536)
+    assert od.threshold(1.0 - 2.0 ** -20) == 2 ** 16 - 1
     with pytest.raises(ValueError):
         od.threshold(1.0)
     n = 512
@@ -51,6 +53,23 @@ def test_threshold_and_keep_fraction():
     # rows, columns and the 4-word grouping are not correlated in an obvious way
     assert abs(z[:, 0::4].mean() - z[:, 3::4].mean()) < 10 * sigma * 2
     assert abs(z[0::2].mean() - z[1::2].mean()) < 10 * sigma * 2
+
+
+def test_keep_mask_element_by_element():
+    """Each element against a scalar evaluation of its definition: one
+    Philox call per (j // 4, i // 2), word j mod 4, low half for even i,
+    high half for odd i."""
+    seed, bh, p = 0xDEAD_BEEF_0123, 2, 0.45
+    t = od.threshold(p)
+    rows, cols = np.arange(6, 11), np.arange(13, 22)
+    z = od.keep_mask(bh, rows, cols, p, seed)
+    for a, i in enumerate(rows):
+        for b, j in enumerate(cols):
+            ctr = tuple(np.array([c], dtype=np.uint64) for c in (j // 4, i // 2, bh, 0))
+            words = od.philox4x32(ctr, (seed % 2 ** 32, seed // 2 ** 32))
+            word = int(words[j % 4][0])
+            half = word & 0xFFFF if i % 2 == 0 else word >> 16
+            assert z[a, b] == (half >= t), (i, j)
 
 
 def test_keep_mask_structure():
