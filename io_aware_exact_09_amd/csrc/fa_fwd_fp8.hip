@@ -8,7 +8,7 @@
 // throughput of the bf16 one:
 //
 //   S^T = K_j Q_i^T       one MFMA per 64-wide d chunk and 32 keys
-//   P~  = 2^(8 + S c_j - m), rounded to E4M3 (P~ <= 2^8 < 448)
+//   P~  = 2^(8 + S c_j - m), rounded to E4M3 (P~ <= 2^8.75 < 448)
 //   O^T += V_j^T P~^T     one MFMA per 32-wide d block and 64 keys
 //
 // Inputs are quantized per block: Q and K carry one fp32 scale per 128-row
@@ -27,7 +27,16 @@
 //   P V: key = 32 h + 8 a + 4 g + x for item e = 16 h + 4 a + x -- the order
 //        in which the S^T accumulators of the tile's two 32-key halves
 //        (register 4a + x of half h) hold P~ -- so lane (d row i, g) of the
-//        V^T tile reads the dwords at key offsets 8 m + 4 g, m = 4 h + a.
+//        V^T tile needs the key dwords 2 m + g, m = 4 h + a.  The V^T tile
+//        is therefore staged with each row's even key dwords first and its
+//        odd ones second (dword-sized direct-to-LDS loads pick the source
+//        dword per lane), and a lane reads its 32 bytes with two 16-byte
+//        reads.
+//
+// Online softmax: the reference max m moves only when a row's tile max
+// exceeds it by more than kLazy8 = 0.75 (log2 units), so P~ <= 2^8.75 stays
+// below the E4M3 maximum (448) and most tiles skip the rescale of O; the key
+// that set m keeps P~ = 2^8, so the row sum stays >= 2^8.
 
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
@@ -47,8 +56,10 @@ __device__ __forceinline__ f32x16 mma_fp8(const i32x8& a, const i32x8& b, f32x16
 }
 
 // Four fp32 values -> four E4M3 bytes (round to nearest even) in one dword.
+// The first conversion writes the low half over the bits of `a` (dead after
+// this), which spares a register clear.
 __device__ __forceinline__ int pack_fp8(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
@@ -64,12 +75,21 @@ struct KTile {
   }
 };
 
-// V^T tile: D rows (d index) of 64 key bytes, chunks swizzled by (r / 4) % 4.
+// V^T tile: D rows (d index) of 64 key bytes.  Logical row layout: the 8
+// even key dwords (keys 8 m .. 8 m + 3), then the 8 odd ones (8 m + 4 ..);
+// its four 16-byte chunks are XOR-swizzled by (r / 4) % 4, so the 16 rows
+// that one ds_read_b128 serves at a time hit 16 different slots of the
+// 256-byte bank window.
 struct VtTile {
   static constexpr int RB = 64;
   __device__ static constexpr int swz(int r) { return (r >> 2) & 3; }
   __device__ static constexpr uint32_t off(int r, int c) {
     return (uint32_t)(r * RB + ((c ^ swz(r)) << 4));
+  }
+  // Key dword of the global row held by LDS dword slot q (0 .. 15) of row r.
+  __device__ static constexpr int key_dword(int r, int q) {
+    const int lq = (((q >> 2) ^ swz(r)) << 2) | (q & 3);   // logical dword
+    return lq < 8 ? 2 * lq : 2 * (lq - 8) + 1;
   }
 };
 
@@ -77,7 +97,7 @@ struct VtTile {
 
 template <int D, bool CAUSAL, bool MASKED>
 __global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(2, 2)))
+__attribute__((amdgpu_waves_per_eu(3, 3)))
 fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
                   const uint8_t* __restrict__ Vt, const float* __restrict__ sQ,
                   const float* __restrict__ sK, const float* __restrict__ sV,
@@ -89,7 +109,8 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
   constexpr int ND = D / 32;               // 32-wide d blocks of O^T
   constexpr int KB = BC * D;               // bytes of the K tile
   constexpr int VB = D * BC;               // bytes of the V^T tile
-  constexpr float kShift = 8.0f;           // P~ = 2^(kShift + s c - m) <= 2^8
+  constexpr float kShift = 8.0f;           // P~ = 2^(kShift + s c - m)
+  constexpr float kLazy8 = 0.75f;          // P~ <= 2^(kShift + kLazy8) < 448
 
   __shared__ __attribute__((aligned(1024))) unsigned char lds0[KB + VB];
   __shared__ __attribute__((aligned(1024))) unsigned char lds1[KB + VB];
@@ -150,12 +171,12 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
     }
     const rsrc_t rv = make_rsrc(Vth + kv0, (uint32_t)((size_t)D * N - kv0));
 #pragma unroll
-    for (int i = 0; i < VB / 1024 / 4; ++i) {
+    for (int i = 0; i < VB / 256 / 4; ++i) {   // one dword per lane, 256 bytes per load
       const int blk = w + 4 * i;
-      const int pos = blk * 1024 + lane * 16;
-      const int r = pos / 64, pc = (pos % 64) >> 4;
-      const uint32_t goff = (uint32_t)r * (uint32_t)N + ((pc ^ VtTile::swz(r)) << 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, as_lds(base + KB + blk * 1024), 16, goff, 0,
+      const int pos = blk * 256 + lane * 4;
+      const int r = pos / 64, q = (pos % 64) >> 2;
+      const uint32_t goff = (uint32_t)r * (uint32_t)N + 4 * VtTile::key_dword(r, q);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, as_lds(base + KB + blk * 256), 4, goff, 0,
                                                0, 0);
     }
   };
@@ -166,9 +187,9 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int x = 0; x < 2; ++x) koff[t][x] = KTile<D>::off(l32, 4 * t + 2 * g + x);
-  uint32_t voff[4];          // chunk cc of row l32: dwords g and g + 2 hold m = 2cc, 2cc+1
+  uint32_t voff[2];          // row l32, logical chunks 2 g and 2 g + 1 (dwords 2 m + g)
 #pragma unroll
-  for (int cc = 0; cc < 4; ++cc) voff[cc] = VtTile::off(l32, cc) + 4 * g;
+  for (int x = 0; x < 2; ++x) voff[x] = VtTile::off(l32, 2 * g + x);
 
   f32x16 oacc[ND];
 #pragma unroll
@@ -217,22 +238,23 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[h][r]);
-    const float m_new = fmaxf(m_run, max_xor32(mx) * cj);
-    if (m_new > m_run) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first kept keys
+    const float m_tile = max_xor32(mx) * cj;
+    const bool grow = m_tile > m_run + kLazy8;
+    if (__any(grow)) {   // wave-uniform branch
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.0f;   // 0 at first
 #pragma unroll
       for (int b = 0; b < ND; ++b) oacc[b] *= alpha;
       l_run *= alpha;
-      m_run = m_new;
+      m_run = grow ? m_tile : m_run;
     }
     const float m_use = (m_run == neg_inf() ? 0.f : m_run) - kShift;
-    float psum[4] = {};
+    float psum[4];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         s[h][r] = __builtin_amdgcn_exp2f(fmaf(s[h][r], cj, -m_use));
-        psum[r & 3] += s[h][r];
+        psum[r & 3] = (h == 0 && r < 4) ? s[h][r] : psum[r & 3] + s[h][r];
       }
     l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
 
@@ -245,17 +267,18 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
         pf[4 * h + a] = pack_fp8(s[h][4 * a], s[h][4 * a + 1], s[h][4 * a + 2], s[h][4 * a + 3]);
 #pragma unroll
     for (int b = 0; b < ND; ++b) {
-      i32x8 av;
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        const unsigned char* p = sVt + voff[cc] + 32 * b * VtTile::RB;
-        av[2 * cc] = *reinterpret_cast<const int*>(p);
-        av[2 * cc + 1] = *reinterpret_cast<const int*>(p + 8);
-      }
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(sVt + voff[0] + 32 * b * VtTile::RB);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(sVt + voff[1] + 32 * b * VtTile::RB);
+      const i32x8 av = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                             (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       oacc[b] = mma_fp8(av, pf, oacc[b]);
     }
   };
 
+  // One loop body with a run-time buffer index: unrolled over the two
+  // buffers, the compiler gave each copy its own registers for the O
+  // accumulators and copied all 64 of them before every P V product; one
+  // body also fits three waves per SIMD (~162 VGPRs at d = 128).
   int j = next_kept(0);
   auto step = [&](auto buf_tag) {
     wait_global_loads();
@@ -266,10 +289,10 @@ fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
     j = jn;
   };
   if (j < ntiles) stage(j, IntTag<0>{});
+  int buf = 0;
   while (j < ntiles) {
-    step(IntTag<0>{});
-    if (j >= ntiles) break;
-    step(IntTag<1>{});
+    step(buf);
+    buf ^= 1;
   }
 
   // ---- epilogue ------------------------------------------------------------------

@@ -131,10 +131,12 @@ def o_error_bound(q8, k8, vt8, sq, sk, sv, scale: float, causal: bool = False,
     """Elementwise bound on |O_gpu - O| from rounding the probabilities to
     E4M3 before the P V product.
 
-    The GPU forms P~_j = 2^(shift + s_j log2 e - m) with m its running max
-    (so the largest kept P~ of a row is 2^shift and the row sum l >= 2^shift),
-    rescales by alpha <= 1 when m moves, and divides by the fp32 row sum of
-    the unrounded P~.  A rounded normal value is within 2^-4 relative, a
+    The GPU forms P~_j = 2^(shift + s_j log2 e - m) with m a reference that
+    trails the running max by less than 0.75 (so a kept P~ is at most
+    2^(shift + 0.75) < 448, still a normal E4M3 value, and the row sum
+    l >= 2^shift, the key that set m contributing 2^shift), rescales by
+    alpha <= 1 when m moves, and divides by the fp32 row sum of the
+    unrounded P~.  A rounded normal value is within 2^-4 relative, a
     subnormal one (below 2^-6) within 2^-10 absolute, so
         |O_gpu - O|_ik <= s_v (2^-4 (P |V8|)_ik + 2^-10 2^-shift sum_j |V8_jk|)
     over kept keys j, V8 the decoded codes.  Returns that bound.
