@@ -70,7 +70,8 @@ HBM_PEAK_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 50; 200 for the short gpt2 and tiny steps)")
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="long")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -86,7 +87,10 @@ def parse():
                     help="skip the two-stream secondary (its staged phases launch the D "
                          "preprocess and a dQ pass that reads D; counter runs leave it out so "
                          "that every dQ launch is the headline's)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.steps is None:   # at least 200 repetitions where a step takes ~0.1 ms
+        args.steps = 200 if args.workload in ("gpt2", "tiny") else 50
+    return args
 
 
 def recorded_traffic(workload, kernel):
