@@ -98,6 +98,23 @@ def keep_mask(bh: int, rows, cols, p: float, seed: int) -> np.ndarray:
     return half >= np.uint64(threshold(p))
 
 
+def _head(q, k, v, do, keep, scale: float, p: float, seed: int, bh: int):
+    """One head (2-D arrays): the formulas of the module docstring with the
+    keep mask of head index bh."""
+    N = q.shape[0]
+    idx = np.arange(N)
+    s = scale * (q @ k.T)
+    s = np.where(keep, s, -np.inf)
+    pr, _, lse = _softmax_rows(s)
+    m = keep_mask(bh, idx, idx, p, seed) * (1.0 / (1.0 - p))
+    o = (pr * m) @ v
+    dv = (pr * m).T @ do
+    dp = (do @ v.T) * m
+    dvec = (do * o).sum(axis=1)
+    ds = pr * (dp - dvec[:, None])
+    return {"O": o, "LSE": lse, "dQ": scale * (ds @ k), "dK": scale * (ds.T @ q), "dV": dv}
+
+
 def forward_backward(q, k, v, do, scale: float, p: float, seed: int, causal: bool = False,
                      block_mask=None, mask_block: int = MASK_BLOCK):
     """Forward and backward of attention with dropout (module docstring).
@@ -107,24 +124,22 @@ def forward_backward(q, k, v, do, scale: float, p: float, seed: int, causal: boo
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     B, H, N, d = q.shape
     keep = keep_matrix(N, N, causal, block_mask, mask_block)
-    inv_keep = 1.0 / (1.0 - p)
     out = {name: np.empty_like(q) for name in ("O", "dQ", "dK", "dV")}
     out["LSE"] = np.empty((B, H, N))
-    idx = np.arange(N)
     for b in range(B):
         for h in range(H):
-            bh = b * H + h
-            s = scale * (q[b, h] @ k[b, h].T)
-            s = np.where(keep, s, -np.inf)
-            pr, _, lse = _softmax_rows(s)
-            m = keep_mask(bh, idx, idx, p, seed) * inv_keep
-            o = (pr * m) @ v[b, h]
-            dv = (pr * m).T @ do[b, h]
-            dp = (do[b, h] @ v[b, h].T) * m
-            dvec = (do[b, h] * o).sum(axis=1)
-            ds = pr * (dp - dvec[:, None])
-            out["O"][b, h], out["LSE"][b, h] = o, lse
-            out["dQ"][b, h] = scale * (ds @ k[b, h])
-            out["dK"][b, h] = scale * (ds.T @ q[b, h])
-            out["dV"][b, h] = dv
+            r = _head(q[b, h], k[b, h], v[b, h], do[b, h], keep, scale, p, seed, b * H + h)
+            for name in out:
+                out[name][b, h] = r[name]
     return out
+
+
+def head_outputs(q, k, v, do, scale: float, p: float, seed: int, b: int, h: int,
+                 causal: bool = False, block_mask=None, mask_block: int = MASK_BLOCK):
+    """The outputs of head (b, h) of [B, H, N, d] inputs alone (full-size
+    checks on a few heads): the per-head step of ``forward_backward``, with
+    the head's own mask index b H + h."""
+    H = q.shape[1]
+    keep = keep_matrix(q.shape[2], q.shape[2], causal, block_mask, mask_block)
+    return _head(_f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h]), _f64(do[b, h]), keep, scale, p,
+                 seed, b * H + h)

@@ -30,11 +30,13 @@ import torch
 
 import oracle
 from oracle import gqa
+from oracle import dropout as od
 from oracle import fp8 as OF
 from io_aware_exact_09_amd import fa
 from io_aware_exact_09_amd import workloads as W
 from gpu_util import device, tol_check, upload, upload_mask
 from test_gpu_fp8 import _check as fp8_check
+from test_gpu_parity import _dq_bar
 
 pytestmark = pytest.mark.gpu
 
@@ -135,6 +137,63 @@ def test_verylong_rows_of_every_head():
     for n in OUTS:
         g, r = np.concatenate(acc[n][0]), np.concatenate(acc[n][1])
         _compare(n, g, r, w, "verylong (sampled rows)", True)
+
+
+def test_long_dropout_two_heads():
+    """The long workload through fa_fwd_dropout / fa_bwd_dropout at p = 0.1
+    with the seed bench.py --dropout 0.1 uses (its launch configuration):
+    heads (0, 0) and (B-1, H-1) whole against the dropout oracle, which
+    regenerates each head's keep mask from the head index."""
+    w = W.WORKLOADS["long"]
+    x = W.make_inputs(w)
+    p, seed = float(np.float32(0.1)), 1234
+    _say(f"workload long with dropout p={p}: B={w.B} H={w.H} N={w.N} d={w.d}")
+    q, k, v, do = (upload(x[n], w.dtype) for n in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    fa.fa_fwd_dropout(q, k, v, o, lse, w.scale, p, seed, w.causal, None)
+    fa.fa_bwd_dropout(q, k, v, o, do, lse, dq, dk, dv, w.scale, p, seed, w.causal, None)
+    torch.cuda.synchronize()
+    got = dict(O=o, LSE=lse, dQ=dq, dK=dk, dV=dv)
+    for b, h in ((0, 0), (w.B - 1, w.H - 1)):
+        ref = od.head_outputs(x["q"], x["k"], x["v"], x["do"], w.scale, p, seed, b, h,
+                              w.causal)
+        label = f"long dropout, head ({b}, {h})"
+        floors = _dropout_floors(x, w, b, h, ref,
+                                 got["O"][b, h].float().cpu().numpy().astype(np.float64))
+        for n in OUTS:
+            g = got[n][b, h].float().cpu().numpy().astype(np.float64)
+            if n not in floors:
+                _compare(n, g, ref[n], w, label, False)
+                continue
+            # dQ and dK take D = rowsum(dO * O) from the O the forward stored
+            # (bf16; with dropout the dropped output): the bar follows the
+            # error that this O alone causes.
+            rel = float(np.linalg.norm(g - ref[n]) / np.linalg.norm(ref[n]))
+            bar = _dq_bar(floors[n])
+            _say(f"  {label} {n}: rel-Fro {rel:.3e} (bf16-O floor {floors[n]:.3e}, bar {bar:.3e})")
+            assert rel <= bar, f"{label} {n} rel-Frobenius {rel:.3e} > {bar:.3e}"
+            max_abs = float(np.abs(g - ref[n]).max())
+            assert max_abs <= 2e-2 * max(1.0, float(np.abs(ref[n]).max())), (n, max_abs)
+
+
+def _dropout_floors(x, w, b, h, ref, o_stored):
+    """dQ and dK errors (rel-Frobenius) that forming D from the stored O
+    (the forward's bf16 output, checked against its own bar above) alone
+    causes: dS changes by -P (D_exact - D_stored) 1^T, P the undropped
+    probabilities (dS = P (dP M - D)), so dQ by scale dS K and dK by
+    scale dS^T Q."""
+    q, k, do = (np.asarray(x[n][b, h], np.float64) for n in ("q", "k", "do"))
+    N = q.shape[0]
+    keep = oracle.keep_matrix(N, N, w.causal)
+    s_ = np.where(keep, w.scale * q @ k.T, -np.inf)
+    pr = np.exp(s_ - ref["LSE"][:, None])
+    d_stored = (do * o_stored).sum(1)
+    d_exact = (do * ref["O"]).sum(1)
+    dds = pr * (d_exact - d_stored)[:, None]
+    return {"dQ": float(np.linalg.norm(w.scale * dds @ k) / np.linalg.norm(ref["dQ"])),
+            "dK": float(np.linalg.norm(w.scale * dds.T @ q) / np.linalg.norm(ref["dK"]))}
 
 
 def test_long_fp8_whole_output():

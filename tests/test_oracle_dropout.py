@@ -87,6 +87,17 @@ def test_keep_mask_structure():
     assert np.all(od.keep_mask(0, rows, cols, 0.0, seed=7))
 
 
+def test_head_outputs_match_whole_tensor():
+    """The one-head helper (full-size checks of a few heads) gives each head
+    exactly what the whole-tensor routine gives it, mask index included."""
+    q, k, v, do = _inputs(2, 3, 20, 4, 8)
+    a = od.forward_backward(q, k, v, do, 0.5, 0.3, 77, causal=True)
+    for b, h in ((0, 0), (1, 2), (0, 2)):
+        r = od.head_outputs(q, k, v, do, 0.5, 0.3, 77, b, h, causal=True)
+        for name in ("O", "LSE", "dQ", "dK", "dV"):
+            assert np.array_equal(r[name], a[name][b, h]), (name, b, h)
+
+
 @pytest.mark.parametrize("causal,use_mask", [(False, False), (True, False), (True, True)])
 def test_p_zero_is_plain_attention(causal, use_mask):
     q, k, v, do = _inputs(1, 2, 48, 8, 1)
