@@ -309,10 +309,12 @@ __device__ __forceinline__ typename Elem<T>::frag gload_frag(rsrc_t r, uint32_t 
 // A tile holds R rows of a [*, D] row-major tensor, unpadded (D * sizeof(T)
 // bytes per row), with the 16-byte chunks of row r stored at chunk position
 // c ^ swz(r).  The swizzles were chosen against the gfx950 LDS, which serves
-// ds_read_b128 16 lanes (256 bytes) at a time and ds_read_b64_tr_b16 32 lanes
-// at a time:
-//   * operand reads along a row (ds_read_b128 by 16 consecutive rows at one
-//     chunk) need swz to be a bijection over 16 consecutive rows;
+// ds_read_b128 in four groups of 16 lanes (256 bytes), grouped by bit 5 and by
+// the parity of bits 2..4 of the lane index (measured with the bank-conflict
+// counter), and ds_read_b64_tr_b16 32 lanes at a time:
+//   * operand reads along a row (ds_read_b128, lane l32 of each half-wave on
+//     row l32 at one chunk; rows r and r + 16 fall in different groups) need
+//     swz to be a bijection over 16 consecutive rows;
 //   * transposed reads (ds_read_b64_tr_b16: 4 consecutive rows x 64 bytes per
 //     32 lanes) need those 4 rows to land in 4 different 64-byte segments of
 //     the 256-byte bank window.
