@@ -324,9 +324,21 @@ def main():
     if grouped and drop > 0:
         print("--dropout is not offered for grouped key/value heads", file=sys.stderr)
         sys.exit(2)
-    phases = ["fwd", "bwd"] if (drop > 0 or grouped) else ["fwd", "dq", "dkdv"]
+    # Shapes whose blocks fill few compute units run the backward split (runs
+    # of tiles with fp32 partials), which only the whole entry points do.
+    split = (not grouped and drop == 0 and w.dtype == "bf16"
+             and fa.fa_bwd_splits(w.B, w.H, w.H, w.N, w.d, w.dtype) != (1, 1))
+    phases = ["fwd", "bwd"] if (drop > 0 or grouped or split) else ["fwd", "dq", "dkdv"]
 
     def step(ev=None):
+        if split:
+            # fa_fwd, then fa_bwd (its kernels in one entry point)
+            if ev: ev[0].record()
+            fa.fa_fwd(q, k, v, o, lse, sc, cz, mask)
+            if ev: ev[1].record()
+            fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, sc, cz, mask, ws)
+            if ev: ev[2].record()
+            return
         if grouped:
             # fa_fwd_gqa, then fa_bwd_gqa (its kernels in one entry point)
             if ev: ev[0].record()
@@ -388,7 +400,8 @@ def main():
     fwd_name = ("fa_fwd_pp_kernel" if w.dtype == "bf16" and w.d == 128 and w.mask_density is None
                 and drop == 0 else "fa_fwd_kernel")
     names = {"fwd": fwd_name, "dkdv": "fa_bwd_dkdv_kernel", "dq": "fa_bwd_dq_kernel",
-             "bwd": ("fa_bwd_gqa" if grouped else "fa_bwd_dropout") + " (all its kernels)"}
+             "bwd": ("fa_bwd_gqa" if grouped else "fa_bwd" if split else "fa_bwd_dropout")
+             + " (all its kernels)"}
     dom = max(phases, key=lambda p: avg[p])
     ach = kflops[dom] / (avg[dom] * 1e-3) / 1e12
     roof = {"kernel": names[dom], "bound": "mfma", "achieved": ach, "peak": peak,

@@ -114,13 +114,42 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
                  const unsigned char* block_mask, fa_dtype dtype, void* stream);
 
 /*
- * fa_bwd_workspace_bytes -- size of the scratch buffer fa_bwd needs: one fp32
+ * fa_bwd_workspace_bytes -- size of the scratch buffer fa_bwd uses: one fp32
  * per query row (D_i = sum_k dO_ik O_ik), i.e. 4 * B * H * N bytes, so the
- * backward's extra memory is O(N) ([FA-guide] "Karmaşıklık Analizi").
- * The size does not depend on the element type.  Returns 0 for sizes that
- * fa_bwd rejects with FA_ERR_SHAPE for either element type.
+ * backward's extra memory is O(N) ([FA-guide] "Karmaşıklık Analizi") --
+ * plus, for shapes whose blocks would fill fewer than the GPU's 256 compute
+ * units (B * H * ceil(N/128) < 256, e.g. one head of a long sequence), the
+ * fp32 partials of the split passes (see fa_bwd_splits): D rounded up to 256
+ * bytes, then 2 * s_kv * B * H * N * d * 4 bytes when s_kv > 1, then
+ * s_q * B * H * N * d * 4 bytes when s_q > 1.  Any workspace of at least
+ * 4 * B * H * N bytes is accepted; with less than this size the passes run
+ * unsplit.  The size does not depend on the element type.  Returns 0 for
+ * sizes that fa_bwd rejects with FA_ERR_SHAPE for either element type.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * fa_bwd_splits -- how fa_bwd, fa_bwd_dropout and fa_bwd_gqa divide the work
+ * of the backward for a shape, given a workspace of the preferred size.
+ * Outputs (host pointers, non-NULL):
+ *   *dkdv_split  work-groups per (key/value head, 128-key block) of the dK/dV
+ *                pass: the group's query heads (grouped heads, as described
+ *                at fa_bwd_gqa) or, with one query head per key/value head,
+ *                runs of its 128-row query tiles;
+ *   *dq_split    work-groups per (query head, 128-row query block) of the dQ
+ *                pass, each taking a run of its 64-key tiles.
+ * Splits apply to bf16 only, where fewer than 256 blocks would run: a split
+ * pass writes fp32 partials into the workspace and a reduction kernel adds
+ * them in a fixed order, so results stay deterministic (but differ in
+ * rounding from the unsplit passes').  At most 8 runs, at least 4 query tiles
+ * (dK/dV) or 8 key tiles (dQ) per run.  The phase entry points
+ * (fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq, fa_bwd_dq_and_d) and
+ * fa_bwd_static never split.
+ * Errors: FA_ERR_NULL, and the shape checks of fa_bwd_gqa (Hq = H, Hkv = H
+ * for the plain backward).
+ */
+fa_status fa_bwd_splits(int B, int Hq, int Hkv, int N, int d, fa_dtype dtype,
+                        int* dkdv_split, int* dq_split);
 
 /*
  * fa_bwd -- gradients of sum(O * dO) with respect to Q, K and V.

@@ -128,7 +128,7 @@ fa_status bwd_impl(const void* Q, const void* K, const void* V, const void* O, c
                    const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int Hkv, int N,
                    int d, float scale, int causal, const unsigned char* block_mask,
                    fa_dtype dtype, void* workspace, size_t workspace_bytes,
-                   const fa::Dropout& drop, void* stream);
+                   const fa::Dropout& drop, void* stream, bool seq_splits = true);
 
 // Key/value head count: >= 1 and dividing the query head count.
 fa_status check_kv_heads(int H, int Hkv) {
@@ -147,15 +147,46 @@ int gqa_split(int B, int H, int Hkv, int N) {
   return (int)std::min<long long>(G, (512 + groups - 1) / groups);
 }
 
-// Backward workspace: D (4 bytes per query row), then, when the grouped
-// dK/dV pass is split, its fp32 partials.
-size_t bwd_workspace(const Shape& s, int Hkv, int* gsplit, size_t* part_off) {
-  const int sp = gqa_split(s.B, s.H, Hkv, s.N);
+// Sequence splits (bf16 only): a shape whose query or key blocks would fill
+// fewer than the 256 compute units of the MI355X (one GPU's share of a long
+// sequence, e.g. one head of 16K rows) gets more work-groups by cutting each
+// key block's query tiles (dK/dV) and each query block's key tiles (dQ) into
+// runs; a run's work-group writes an fp32 partial and a reduction kernel adds
+// the partials in a fixed order, so results stay deterministic.  The split
+// count aims at `target` work-groups, at most 8 runs and at least `min_run`
+// tiles per run.
+constexpr int kCUs = 256;
+
+int run_split(long long blocks, long long target, int tiles, int min_run) {
+  if (blocks >= kCUs) return 1;
+  long long sp = std::min<long long>((target + blocks - 1) / blocks, 8);
+  sp = std::min<long long>(sp, std::max(1, tiles / min_run));
+  return (int)std::max<long long>(1, sp);
+}
+
+// Backward work split and workspace layout: D (4 bytes per query row,
+// rounded up to 256 bytes), then the dK/dV partials, then the dQ partials.
+struct BwdPlan {
+  int kv = 1, q = 1;            // dK/dV split (grouped heads or query tiles), dQ split
+  size_t kv_off = 0, q_off = 0;
+  size_t bytes = 0;             // workspace needed
+};
+
+BwdPlan bwd_plan(const Shape& s, int Hkv, bool seq_splits) {
+  BwdPlan p;
+  p.kv = gqa_split(s.B, s.H, Hkv, s.N);
+  if (seq_splits && s.dtype == FA_BF16) {
+    const int nb = (s.N + 127) / 128;
+    if (Hkv == s.H)             // one query head per key/value head
+      p.kv = run_split((long long)s.B * s.H * nb, 2LL * kCUs * (s.d == 64 ? 2 : 1), nb, 4);
+    p.q = run_split((long long)s.B * s.H * nb, 4LL * kCUs, (s.N + 63) / 64, 8);
+  }
   const size_t rows = ((size_t)s.row_bytes() + 255) / 256 * 256;
-  if (gsplit) *gsplit = sp;
-  if (part_off) *part_off = rows;
-  if (sp == 1) return (size_t)s.row_bytes();
-  return rows + (size_t)2 * sp * s.B * Hkv * s.N * s.d * 4;
+  p.kv_off = rows;
+  p.q_off = rows + (p.kv > 1 ? (size_t)2 * p.kv * s.B * Hkv * s.N * s.d * 4 : 0);
+  const size_t qb = p.q > 1 ? (size_t)p.q * s.B * s.H * s.N * s.d * 4 : 0;
+  p.bytes = (p.kv == 1 && p.q == 1) ? (size_t)s.row_bytes() : p.q_off + qb;
+  return p;
 }
 
 }  // namespace
@@ -213,7 +244,19 @@ fa_status fwd_impl(const void* Q, const void* K, const void* V, void* O, float* 
 FA_EXPORT size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   const Shape s{B, H, N, d, FA_BF16};
   if (check_shape(s, 1.0f) != FA_OK) return 0;
-  return (size_t)s.row_bytes();
+  return bwd_plan(s, H, true).bytes;
+}
+
+FA_EXPORT fa_status fa_bwd_splits(int B, int Hq, int Hkv, int N, int d, fa_dtype dtype,
+                                  int* dkdv_split, int* dq_split) {
+  if (!dkdv_split || !dq_split) return FA_ERR_NULL;
+  const Shape s{B, Hq, N, d, dtype};
+  FA_TRY(check_shape(s, 1.0f));
+  FA_TRY(check_kv_heads(Hq, Hkv));
+  const BwdPlan p = bwd_plan(s, Hkv, true);
+  *dkdv_split = p.kv;
+  *dq_split = p.q;
+  return FA_OK;
 }
 
 FA_EXPORT fa_status fa_bwd_preprocess(const void* O, const void* dO, int B, int H, int N, int d,
@@ -315,7 +358,8 @@ FA_EXPORT fa_status fa_bwd_static(const void* Q, const void* K, const void* V, c
   void* ws = nullptr;
   if (fa::static_scratch(&ws) != hipSuccess) return FA_ERR_LAUNCH;
   return bwd_impl(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, H, N, d, scale, causal, block_mask,
-                  dtype, ws, FA_STATIC_SCRATCH_BYTES, fa::Dropout{}, stream);
+                  dtype, ws, FA_STATIC_SCRATCH_BYTES, fa::Dropout{}, stream,
+                  /*seq_splits=*/false);
 }
 
 FA_EXPORT fa_status fa_bwd_dropout(const void* Q, const void* K, const void* V, const void* O,
@@ -336,7 +380,7 @@ FA_EXPORT fa_status fa_bwd_dropout(const void* Q, const void* K, const void* V, 
 FA_EXPORT size_t fa_bwd_gqa_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
   const Shape s{B, Hq, N, d, FA_BF16};
   if (check_shape(s, 1.0f) != FA_OK || check_kv_heads(Hq, Hkv) != FA_OK) return 0;
-  return bwd_workspace(s, Hkv, nullptr, nullptr);
+  return bwd_plan(s, Hkv, true).bytes;
 }
 
 FA_EXPORT fa_status fa_fwd_gqa(const void* Q, const void* K, const void* V, void* O, float* LSE,
@@ -361,7 +405,7 @@ fa_status bwd_impl(const void* Q, const void* K, const void* V, const void* O, c
                    const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int Hkv, int N,
                    int d, float scale, int causal, const unsigned char* block_mask,
                    fa_dtype dtype, void* workspace, size_t workspace_bytes,
-                   const fa::Dropout& drop, void* stream) {
+                   const fa::Dropout& drop, void* stream, bool seq_splits) {
   FA_TRY(check_buffers({{Q, 0, 0}, {K, 0, 0}, {V, 0, 0}, {O, 0, 0}, {dO, 0, 0}, {LSE, 0, 0}},
                        {{dQ, 0, 0}, {dK, 0, 0}, {dV, 0, 0}}));
   const Shape s{B, H, N, d, dtype};
@@ -369,9 +413,13 @@ fa_status bwd_impl(const void* Q, const void* K, const void* V, const void* O, c
   FA_TRY(check_kv_heads(H, Hkv));
   const uintptr_t tb = s.tensor_bytes(), lb = s.row_bytes();
   const uintptr_t kvb = tb / H * Hkv;
-  int gsplit = 1;
-  size_t part_off = 0;
-  const size_t need = bwd_workspace(s, Hkv, &gsplit, &part_off);
+  // The sequence splits are used when the workspace holds their partials
+  // (fa_bwd_workspace_bytes and fa_bwd_gqa_workspace_bytes include them);
+  // with less, down to D alone, the passes run unsplit.  The grouped-head
+  // split of dK/dV is required.
+  BwdPlan plan = bwd_plan(s, Hkv, seq_splits);
+  if (seq_splits && workspace_bytes < plan.bytes) plan = bwd_plan(s, Hkv, false);
+  const size_t need = plan.bytes;
   const Buf ws{workspace, workspace_bytes, 16};
   const Buf m{block_mask, block_mask ? s.mask_bytes() : 0, 1};
   FA_TRY(check_layout(
@@ -380,8 +428,10 @@ fa_status bwd_impl(const void* Q, const void* K, const void* V, const void* O, c
 
   fa::BwdArgs a = bwd_args(s, scale, causal, block_mask, stream);
   a.G = H / Hkv;
-  a.gsplit = gsplit;
-  if (gsplit > 1) a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_off);
+  a.gsplit = plan.kv;
+  if (plan.kv > 1) a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.kv_off);
+  a.ksplit = plan.q;
+  if (plan.q > 1) a.qpart = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.q_off);
   a.q = Q; a.k = K; a.v = V; a.o = O; a.dout = dO; a.lse = LSE;
   a.dq = dQ; a.dk = dK; a.dv = dV;
   a.delta = static_cast<float*>(workspace);

@@ -170,9 +170,17 @@ fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   };
 
   // The walk covers (query head of the group, staged tile) pairs u =
-  // gq * ntiles + i, kept tiles only.
-  const int U0 = (sp * kv_group / gsplit) * ntiles;
-  const int NU = ((sp + 1) * kv_group / gsplit) * ntiles;
+  // gq * ntiles + i, tiles from the causal start `first` on, kept tiles only.
+  // With gsplit > 1 the kv_group * (ntiles - first) pairs are cut into
+  // gsplit equal runs, one per work-group: whole query heads when gsplit
+  // divides kv_group, else runs of one head's query tiles.
+  const int nt = ntiles - first;
+  const int tot = kv_group * nt;
+  auto u_at = [&](int idx) {
+    return idx >= tot ? kv_group * ntiles : (idx / nt) * ntiles + first + idx % nt;
+  };
+  const int U0 = u_at((int)((long long)sp * tot / gsplit));
+  const int NU = u_at((int)((long long)(sp + 1) * tot / gsplit));
   auto next_u = [&](int u) {
     while (u < NU) {
       const int gq = u / ntiles;
@@ -611,6 +619,20 @@ fa_bwd_dkdv_reduce_kernel(const float* __restrict__ part, T* __restrict__ dK,
   }
 }
 
+// dQ = the sum of the ksplit fp32 partials of the dQ pass, in split order.
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+fa_bwd_dq_reduce_kernel(const float* __restrict__ part, T* __restrict__ dQ,
+                        size_t E4 /* elements / 4 */, int ksplit) {
+  const f32x4* p = reinterpret_cast<const f32x4*>(part);
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < E4;
+       i += (size_t)gridDim.x * blockDim.x) {
+    f32x4 q = p[i];
+    for (int sp = 1; sp < ksplit; ++sp) q += p[(size_t)sp * E4 + i];
+    Elem<T>::store4(dQ + 4 * i, q[0], q[1], q[2], q[3]);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 3. dQ: work-group = 128 queries (wave w: rows 32w..32w+31, lane pair one
 //    row), same walk over key tiles as the forward:
@@ -676,7 +698,7 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
                  const T* __restrict__ dO, const T* __restrict__ O, const float* __restrict__ LSE,
                  float* __restrict__ delta, T* __restrict__ dQ,
                  const uint8_t* __restrict__ mask, int BH, int kv_group, int N, int T_tiles,
-                 float c, float scale, DropParams drp) {
+                 float c, float scale, DropParams drp, int ksplit, float* __restrict__ qpart) {
   using E = Elem<T>;
   using frag = typename E::frag;
   using Cfg = DqCfg<T>;
@@ -692,8 +714,12 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
   const int nqb = (N + BR - 1) / BR;
-  const BlockCoord bc = map_block(blockIdx.x, nqb, BH, CAUSAL, true);
-  const int bh = bc.bh, q0 = bc.blk * BR;
+  // With ksplit > 1 each query block's key tiles are cut into ksplit runs
+  // of equal length, one per work-group, which write scale * their dQ
+  // partial in fp32 (qpart, [ksplit][BH * N * D]) for a reduction kernel;
+  // the runs of one block count as separate heads in the block order.
+  const BlockCoord bc = map_block(blockIdx.x, nqb, BH * ksplit, CAUSAL, true);
+  const int bh = bc.bh / ksplit, ksp = bc.bh - bh * ksplit, q0 = bc.blk * BR;
   const size_t head = (size_t)bh * N * D;
   const size_t kvhead = (size_t)(bh / kv_group) * N * D;    // shared key/value head
   const T* Kh = K + kvhead;
@@ -731,7 +757,9 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   }
 
   const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
-  const int ntiles = (kv_end + BC - 1) / BC;
+  const int ntiles_all = (kv_end + BC - 1) / BC;
+  const int jbeg = (int)((long long)ksp * ntiles_all / ksplit);
+  const int ntiles = (int)((long long)(ksp + 1) * ntiles_all / ksplit);   // end of this run
   KeptTiles<BC> kept(MASKED ? mask + (size_t)(q0 / kMaskBlock) * T_tiles : nullptr, 1, T_tiles);
   auto next_kept = [&](int j) {
     if constexpr (MASKED) return kept.next(j, lane);
@@ -755,13 +783,13 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   constexpr bool USE_LO = sizeof(T) == 2;
   LaneOffsets<T, D> lo;
   if constexpr (USE_LO) lo.init(lane);
-  int j = next_kept(0);
+  int j = next_kept(jbeg);
   if (j < ntiles) stage(j, IntTag<0>{});
   wait_global_loads();
   const float lse2 = (qrow < N && lrow != neg_inf()) ? lrow * kLog2e : pos_inf();
   if (O) {
     dval = pair_row_delta<T, D>(oo, of);
-    if (g == 0 && qrow < N) delta[(size_t)bh * N + qrow] = dval;
+    if (ksp == 0 && g == 0 && qrow < N) delta[(size_t)bh * N + qrow] = dval;
   }
   // Starting value of every dP accumulator: -D (times 1 - p under dropout),
   // so the matrix cores return dP - D and the tile needs no subtraction.
@@ -937,6 +965,19 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
     }
   }
 
+  if (ksplit > 1) {
+    if (qrow < N) {
+      float* pr = qpart + (size_t)ksp * BH * N * D + head + (size_t)qrow * D;
+#pragma unroll
+      for (int b = 0; b < ND; ++b)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          *reinterpret_cast<f32x4*>(pr + 32 * b + 8 * a + 4 * g) =
+              f32x4{dqacc[b][4 * a], dqacc[b][4 * a + 1], dqacc[b][4 * a + 2],
+                    dqacc[b][4 * a + 3]} * scale;
+    }
+    return;
+  }
   if constexpr (sizeof(T) == 2) {
     // Results through LDS (fa_rows.hpp; padded rows would not fit).
     static_assert(BR * D * (int)sizeof(T) <= 2 * TB, "result rows must fit a staging array");
@@ -1008,15 +1049,21 @@ template <typename T, int D, bool CAUSAL, bool MASKED>
 static hipError_t launch_dq_t(const BwdArgs& a) {
   const int nqb = (a.N + DqCfg<T>::BR - 1) / DqCfg<T>::BR;
   auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3(nqb * a.BH), dim3(kThreads), 0, a.stream,
+    hipLaunchKernelGGL(kernel, dim3(nqb * a.BH * a.ksplit), dim3(kThreads), 0, a.stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), static_cast<const T*>(a.dout),
                        a.dq_forms_delta ? static_cast<const T*>(a.o) : nullptr, a.lse, a.delta,
                        static_cast<T*>(a.dq), a.mask, a.BH, a.G, a.N, a.T, score_coef(a.scale),
-                       a.scale, drop_params(a));
+                       a.scale, drop_params(a), a.ksplit, a.qpart);
   };
   if (a.drop.on) go(fa_bwd_dq_kernel<T, D, CAUSAL, MASKED, true>);
   else go(fa_bwd_dq_kernel<T, D, CAUSAL, MASKED, false>);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.ksplit == 1) return e;
+  const size_t E4 = (size_t)a.BH * a.N * D / 4;
+  const unsigned blocks = (unsigned)std::min<size_t>((E4 + kThreads - 1) / kThreads, 4096);
+  hipLaunchKernelGGL((fa_bwd_dq_reduce_kernel<T>), dim3(blocks), dim3(kThreads), 0, a.stream,
+                     a.qpart, static_cast<T*>(a.dq), E4, a.ksplit);
   return hipGetLastError();
 }
 

@@ -40,8 +40,11 @@ struct BwdArgs {
   const uint8_t* mask;
   int BH, N, d, T;         // BH = B * (query heads)
   int G = 1;               // query heads per key/value head (K, V, dK, dV have BH / G heads)
-  int gsplit = 1;          // work-groups sharing one key/value head's query heads in dK/dV
+  int gsplit = 1;          // work-groups sharing one key/value head's (query head, query
+                           // tile) pairs in dK/dV
   float* part = nullptr;   // fp32 dK, dV partials, [2][gsplit][BH / G * N * d] (gsplit > 1)
+  int ksplit = 1;          // work-groups sharing one query block's key tiles in dQ
+  float* qpart = nullptr;  // fp32 dQ partials, [ksplit][BH * N * d] (ksplit > 1)
   float scale;
   bool causal, bf16;
   Dropout drop;

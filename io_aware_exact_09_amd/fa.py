@@ -60,6 +60,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp]
         lib.fa_fwd.restype = i
         lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
+        lib.fa_bwd_splits.argtypes = [i, i, i, i, i, i, ctypes.POINTER(ctypes.c_int),
+                                      ctypes.POINTER(ctypes.c_int)]
+        lib.fa_bwd_splits.restype = ctypes.c_int
         lib.fa_bwd_workspace_bytes.restype = sz
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i,
                                vp, sz, vp]
@@ -163,6 +166,16 @@ def _scratch(nbytes: int, ref: torch.Tensor, stream=None) -> torch.Tensor:
 
 def fa_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
     return int(load_library().fa_bwd_workspace_bytes(B, H, N, d))
+
+
+def fa_bwd_splits(B: int, Hq: int, Hkv: int, N: int, d: int, dtype: str) -> tuple[int, int]:
+    """(dK/dV split, dQ split) that fa_bwd / fa_bwd_gqa / fa_bwd_dropout use
+    for this shape with a workspace of the preferred size."""
+    kv, q = ctypes.c_int(0), ctypes.c_int(0)
+    code = {"bf16": 0, "fp32": 1}[dtype]
+    _check(load_library().fa_bwd_splits(B, Hq, Hkv, N, d, code, ctypes.byref(kv),
+                                        ctypes.byref(q)), "fa_bwd_splits")
+    return kv.value, q.value
 
 
 def fa_fwd(q, k, v, o, lse, scale: float, causal: bool = False, block_mask=None,

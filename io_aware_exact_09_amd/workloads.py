@@ -18,6 +18,8 @@ The five workloads stand in for the shapes the FlashAttention reading guide
   long_gqa  as long (1% of K rows x20), 4 key/value heads shared by the
             16 query heads
   long_fp8  as long, quantized to FP8 (E4M3) for the FP8 forward
+  verylong_shard  B=1 H=1 N=16384 d=128 bf16 causal sigma = 0.5: one GPU's
+            share of verylong split by heads over eight GPUs
 
 Recipe (the same for every workload): ``rng = numpy.random.default_rng(seed)``
 (PCG64); draw Q, K, V, dO in that order, each
@@ -95,6 +97,10 @@ WORKLOADS = {
     # the long-context shape without the causal mask (every query row sees
     # every key, as in an encoder), iid N(0, 1) inputs
     "long_nc": Workload("long_nc", 2, 16, 4096, 128, "bf16", False, seed=1008),
+    # one GPU's share of verylong when its eight heads are split over eight
+    # GPUs (heads are independent): one head of 16K rows, drawn as verylong
+    "verylong_shard": Workload("verylong_shard", 1, 1, 16384, 128, "bf16", True,
+                               sigma=0.5, seed=1009),
 }
 
 

@@ -34,7 +34,7 @@ def test_header_symbols_are_exported(lib):
                           "fa_fwd_dropout", "fa_bwd_dropout", "fa_decode", "fa_fwd_gqa",
                           "fa_bwd_gqa", "fa_fwd_fp8", "fa_bwd_gqa_workspace_bytes",
                           "fa_decode_num_splits", "fa_decode_workspace_bytes",
-                          "fa_bwd_static", "fa_bwd_dq_and_d"}
+                          "fa_bwd_static", "fa_bwd_dq_and_d", "fa_bwd_splits"}
     out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -52,7 +52,31 @@ def test_status_strings(lib):
     assert fa.status_str(42) == "unknown status"
 
 
+def test_bwd_splits(lib):
+    # enough blocks (B*H*ceil(N/128) >= 256): no split
+    assert fa.fa_bwd_splits(2, 16, 16, 4096, 128, "bf16") == (1, 1)
+    assert fa.fa_bwd_splits(8, 12, 12, 1024, 64, "bf16") == (1, 1)
+    # one head of 16K rows (128 blocks): dK/dV runs of 32 query tiles, dQ runs of 32 key tiles
+    assert fa.fa_bwd_splits(1, 1, 1, 16384, 128, "bf16") == (4, 8)
+    # d = 64 runs two dK/dV work-groups per compute unit, so it aims at twice as many
+    assert fa.fa_bwd_splits(1, 1, 1, 16384, 64, "bf16") == (8, 8)
+    # short rows: capped by the tiles per run (4 query tiles, 8 key tiles)
+    assert fa.fa_bwd_splits(1, 1, 1, 1024, 128, "bf16") == (2, 2)
+    assert fa.fa_bwd_splits(1, 2, 2, 300, 128, "bf16") == (1, 1)
+    # fp32 never splits; grouped heads keep their head split for dK/dV
+    assert fa.fa_bwd_splits(1, 1, 1, 16384, 128, "fp32") == (1, 1)
+    assert fa.fa_bwd_splits(2, 16, 4, 4096, 128, "bf16") == (2, 1)
+    with pytest.raises(RuntimeError):
+        fa.fa_bwd_splits(1, 6, 4, 100, 64, "bf16")
+    st = lib.fa_bwd_splits(1, 1, 1, 128, 64, 0, None, None)
+    assert st == 1      # FA_ERR_NULL
+
+
 def test_workspace_bytes(lib):
+    # one head of 16K rows: D, then the dK/dV partials (4 runs), then dQ's (8 runs)
+    rows = 4 * 16384
+    assert fa.fa_bwd_workspace_bytes(1, 1, 16384, 128) == rows + 2 * 4 * 16384 * 128 * 4 \
+        + 8 * 16384 * 128 * 4
     assert fa.fa_bwd_workspace_bytes(2, 16, 4096, 128) == 4 * 2 * 16 * 4096
     assert fa.fa_bwd_workspace_bytes(1, 8, 16384, 128) == 4 * 8 * 16384
     assert fa.fa_bwd_workspace_bytes(1, 1, 1, 64) == 4

@@ -125,6 +125,23 @@ def test_small_against_dropout_oracle(N, d, dtype, causal, mk, p):
         _say(f"  {n}: " + " ".join(f"{k}={v:.3e}" for k, v in e.items()))
 
 
+def test_split_passes_with_dropout():
+    """One head of 2048 rows splits both backward passes (runs of tiles
+    with fp32 partials); the keep mask depends only on absolute positions."""
+    B, H, N, d, p = 1, 1, 2048, 128, 0.1
+    kv, qs = fa.fa_bwd_splits(B, H, H, N, d, "bf16")
+    _say(f"splits dK/dV {kv}, dQ {qs}")
+    assert kv > 1 and qs > 1
+    inp = W.random_inputs(B, H, N, d, "bf16", seed=77)
+    scale = 1.0 / math.sqrt(d)
+    got = run_dropout(inp, "bf16", scale, True, None, p, 4321)
+    ref = od.forward_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, _f32(p), 4321,
+                              True, None)
+    for n in OUTS:
+        e = tol_check(n, got[n], ref[n], "bf16")
+        _say(f"  {n}: " + " ".join(f"{k}={v:.3e}" for k, v in e.items()))
+
+
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp32", 64)])
 def test_negative_scale(dtype, d):
     """Any finite scale: dropout with a negative one against the oracle."""

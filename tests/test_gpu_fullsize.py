@@ -109,6 +109,30 @@ def test_workload_whole_tensors(name):
         _compare(n, got[n], ref[n], w, name, name in LITERAL)
 
 
+def test_verylong_shard_rows():
+    """One GPU's share of verylong split by heads (B=1, H=1, N=16384): the
+    backward runs split (dK/dV 4 runs of query tiles, dQ 8 runs of key
+    tiles); 1024 query and 1024 key rows against the row oracle."""
+    w = W.WORKLOADS["verylong_shard"]
+    assert fa.fa_bwd_splits(w.B, w.H, w.H, w.N, w.d, "bf16") == (4, 8)
+    x = W.make_inputs(w)
+    _say(f"workload verylong_shard: B={w.B} H={w.H} N={w.N} d={w.d}")
+    got = _run_workload(w, x)
+    rng = np.random.default_rng(29)
+    fixed = np.array([0, 1, 63, 64, 127, 128, 255, 256, w.N // 2, w.N - 129, w.N - 128,
+                      w.N - 1])
+    rows = np.unique(np.concatenate([fixed, rng.choice(w.N, size=1024, replace=False)]))
+    qr = oracle.query_rows(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], x["do"][0, 0], w.scale,
+                           rows, w.causal)
+    kr = oracle.key_rows(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], x["do"][0, 0], w.scale,
+                         rows, w.causal)
+    ref = {**qr, **kr}
+    idx = torch.from_numpy(rows).to(device())
+    for n in OUTS:
+        g = got[n][0, 0][idx].float().cpu().numpy().astype(np.float64)
+        _compare(n, g, ref[n], w, "verylong_shard (sampled rows)", True)
+
+
 def test_verylong_rows_of_every_head():
     """B=1, H=8, N=16384, d=128, causal, sigma 0.5: 512 query rows (O, LSE,
     dQ) and 512 key rows (dK, dV) of every head, always including the first

@@ -60,6 +60,8 @@ SMALL = [
     (1, 6, 2, 200, 128, "bf16", False, None),
     (2, 6, 3, 200, 64, "fp32", True, None),
     (1, 8, 1, 129, 128, "fp32", False, None),
+    # few blocks: dK/dV splits by query head, dQ by runs of key tiles
+    (1, 4, 1, 2048, 128, "bf16", True, None),
 ]
 
 

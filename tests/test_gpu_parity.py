@@ -71,6 +71,50 @@ def test_small_against_full_oracle(N, d, dtype, causal, mk):
     check_all(got, ref, dtype, f"N={N}")
 
 
+# --------------------------------------------------------------------------
+# Split passes: a shape whose blocks fill few compute units (one head of a
+# long sequence) runs dK/dV as runs of query tiles and dQ as runs of key
+# tiles, each writing fp32 partials that a reduction kernel adds.
+# --------------------------------------------------------------------------
+
+SPLIT = [
+    # (B, H, N, d, causal, mask-kind)
+    (1, 1, 4096, 128, True, None),
+    (1, 1, 3000, 128, False, None),
+    (1, 2, 2048, 64, True, "rand"),
+    (1, 1, 2560, 64, False, None),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,mk", SPLIT,
+                         ids=[f"B{a}-H{b}-N{c}-d{e}-{'causal' if f else 'dense'}-{g or 'nomask'}"
+                              for a, b, c, e, f, g in SPLIT])
+def test_split_backward_against_oracle(B, H, N, d, causal, mk):
+    """The split passes against the full oracle, and against the unsplit
+    backward (fa_bwd_static never splits) on the same O and LSE."""
+    kv, qs = fa.fa_bwd_splits(B, H, H, N, d, "bf16")
+    _say(f"case B={B} H={H} N={N} d={d} causal={causal} mask={mk}: splits dK/dV {kv}, dQ {qs}")
+    assert kv > 1 and qs > 1
+    inp = W.random_inputs(B, H, N, d, "bf16", seed=N + d)
+    mask = W.random_block_mask(N, 0.6, seed=N) if mk == "rand" else None
+    scale = 1.0 / math.sqrt(d)
+    q, k, v, do = (upload(inp[n], "bf16") for n in ("q", "k", "v", "do"))
+    m = upload_mask(mask)
+    o, lse = fa.forward(q, k, v, scale, causal, m)
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, scale, causal, m)
+    un = [torch.empty_like(t) for t in (dq, dk, dv)]
+    fa.fa_bwd_static(q, k, v, o, do, lse, *un, scale, causal, m)
+    torch.cuda.synchronize()
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
+    got = dict(O=f64(o), LSE=f64(lse), dQ=f64(dq), dK=f64(dk), dV=f64(dv))
+    ref = oracle.forward_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, causal, mask)
+    check_all(got, ref, "bf16", "split")
+    for n, a, b in zip(("dQ", "dK", "dV"), (dq, dk, dv), un):
+        diff = float((a.float() - b.float()).abs().max())
+        _say(f"  split vs unsplit {n}: max-abs {diff:.3e}")
+        tol_check(n, f64(a), f64(b), "bf16")
+
+
 def test_fully_masked_rows():
     """A mask that drops a diagonal tile under causal masking leaves query
     rows with no key: O = 0, LSE = -inf, dQ = 0, nothing NaN."""
