@@ -329,12 +329,19 @@ def main():
     split = (not grouped and drop == 0 and w.dtype == "bf16"
              and fa.fa_bwd_splits(w.B, w.H, w.H, w.N, w.d, w.dtype) != (1, 1))
     phases = ["fwd", "bwd"] if (drop > 0 or grouped or split) else ["fwd", "dq", "dkdv"]
+    # ... and the forward in runs of key tiles, with a workspace
+    fwd_ws_bytes = fa.fa_fwd_workspace_bytes(w.B, w.H, w.N, w.d) \
+        if (split and mask is None) else 0
+    fws = torch.empty(fwd_ws_bytes, dtype=torch.uint8, device=dev) if fwd_ws_bytes else None
 
     def step(ev=None):
         if split:
-            # fa_fwd, then fa_bwd (its kernels in one entry point)
+            # fa_fwd_ws (its kernels), then fa_bwd (its kernels in one entry point)
             if ev: ev[0].record()
-            fa.fa_fwd(q, k, v, o, lse, sc, cz, mask)
+            if fws is not None:
+                fa.fa_fwd_ws(q, k, v, o, lse, sc, cz, mask, fws)
+            else:
+                fa.fa_fwd(q, k, v, o, lse, sc, cz, mask)
             if ev: ev[1].record()
             fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, sc, cz, mask, ws)
             if ev: ev[2].record()
@@ -399,6 +406,8 @@ def main():
     # forward kernel, everything else on the four-wave one.
     fwd_name = ("fa_fwd_pp_kernel" if w.dtype == "bf16" and w.d == 128 and w.mask_density is None
                 and drop == 0 else "fa_fwd_kernel")
+    if fws is not None:
+        fwd_name = "fa_fwd_ws (all its kernels)"
     names = {"fwd": fwd_name, "dkdv": "fa_bwd_dkdv_kernel", "dq": "fa_bwd_dq_kernel",
              "bwd": ("fa_bwd_gqa" if grouped else "fa_bwd" if split else "fa_bwd_dropout")
              + " (all its kernels)"}

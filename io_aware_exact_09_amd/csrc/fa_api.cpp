@@ -122,7 +122,7 @@ fa_status dropout_params(float p, unsigned long long seed, fa::Dropout* out) {
 fa_status fwd_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
                    int H, int Hkv, int N, int d, float scale, int causal,
                    const unsigned char* block_mask, fa_dtype dtype, const fa::Dropout& drop,
-                   void* stream);
+                   void* stream, void* workspace = nullptr, size_t workspace_bytes = 0);
 
 fa_status bwd_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                    const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int Hkv, int N,
@@ -189,6 +189,27 @@ BwdPlan bwd_plan(const Shape& s, int Hkv, bool seq_splits) {
   return p;
 }
 
+// Forward split (the ping-pong kernel: bf16, d = 128, no block mask, no
+// dropout): with fewer than 256 blocks of 256 query rows, each block's key
+// tiles are cut into runs (at most 8, at least 8 tiles of 64 keys each),
+// aiming at 512 work-groups; the runs' fp32 O and LSE go to the workspace
+// (O first, then LSE) and a combine kernel merges them in run order.
+struct FwdPlan {
+  int runs = 1;
+  size_t lse_off = 0, bytes = 0;   // bytes = 0: no split
+};
+
+FwdPlan fwd_plan(const Shape& s, bool masked, bool dropout) {
+  FwdPlan p;
+  if (s.dtype != FA_BF16 || s.d != 128 || masked || dropout) return p;
+  p.runs = run_split((long long)s.B * s.H * ((s.N + 255) / 256), 2LL * kCUs, (s.N + 63) / 64, 8);
+  if (p.runs == 1) return p;
+  const size_t rows = (size_t)s.B * s.H * s.N;
+  p.lse_off = (size_t)p.runs * rows * s.d * 4;
+  p.bytes = p.lse_off + (size_t)p.runs * rows * 4;
+  return p;
+}
+
 }  // namespace
 
 FA_EXPORT fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
@@ -196,6 +217,21 @@ FA_EXPORT fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O,
                            const unsigned char* block_mask, fa_dtype dtype, void* stream) {
   return fwd_impl(Q, K, V, O, LSE, B, H, H, N, d, scale, causal, block_mask, dtype,
                   fa::Dropout{}, stream);
+}
+
+FA_EXPORT size_t fa_fwd_workspace_bytes(int B, int H, int N, int d) {
+  const Shape s{B, H, N, d, FA_BF16};
+  if (check_shape(s, 1.0f) != FA_OK) return 0;
+  return fwd_plan(s, false, false).bytes;
+}
+
+FA_EXPORT fa_status fa_fwd_ws(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                              int B, int H, int N, int d, float scale, int causal,
+                              const unsigned char* block_mask, fa_dtype dtype, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!workspace && workspace_bytes) return FA_ERR_WORKSPACE;
+  return fwd_impl(Q, K, V, O, LSE, B, H, H, N, d, scale, causal, block_mask, dtype,
+                  fa::Dropout{}, stream, workspace, workspace_bytes);
 }
 
 FA_EXPORT fa_status fa_fwd_dropout(const void* Q, const void* K, const void* V, void* O,
@@ -215,7 +251,7 @@ namespace {
 fa_status fwd_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
                    int H, int Hkv, int N, int d, float scale, int causal,
                    const unsigned char* block_mask, fa_dtype dtype, const fa::Dropout& drop,
-                   void* stream) {
+                   void* stream, void* workspace, size_t workspace_bytes) {
   FA_TRY(check_buffers({{Q, 0, 0}, {K, 0, 0}, {V, 0, 0}}, {{O, 0, 0}, {LSE, 0, 0}}));
   const Shape s{B, H, N, d, dtype};
   FA_TRY(check_shape(s, scale));
@@ -224,7 +260,12 @@ fa_status fwd_impl(const void* Q, const void* K, const void* V, void* O, float* 
   const uintptr_t kvb = tb / H * Hkv;
   const Buf q{Q, tb, 16}, k{K, kvb, 16}, v{V, kvb, 16}, o{O, tb, 16}, l{LSE, lb, 4};
   const Buf m{block_mask, block_mask ? s.mask_bytes() : 0, 1};
-  FA_TRY(check_layout({q, k, v, m}, {o, l}, nullptr, false, 0));
+  // A workspace, when given, is checked like any output (alignment, no
+  // overlap); the run split is used when it is large enough.
+  const Buf ws{workspace, workspace_bytes, 16};
+  FA_TRY(check_layout({q, k, v, m}, {o, l}, workspace ? &ws : nullptr, true, 0));
+  const FwdPlan plan = fwd_plan(s, block_mask != nullptr, drop.on);
+  const bool split = workspace && plan.bytes && workspace_bytes >= plan.bytes;
 
   fa::FwdArgs a{};
   a.q = Q; a.k = K; a.v = V; a.o = O; a.lse = LSE;
@@ -236,6 +277,11 @@ fa_status fwd_impl(const void* Q, const void* K, const void* V, void* O, float* 
   a.bf16 = dtype == FA_BF16;
   a.drop = drop;
   a.stream = static_cast<hipStream_t>(stream);
+  if (split) {
+    a.fsplit = plan.runs;
+    a.opart = static_cast<float*>(workspace);
+    a.lpart = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.lse_off);
+  }
   return fa::launch_fwd(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

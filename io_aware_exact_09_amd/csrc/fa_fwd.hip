@@ -341,7 +341,8 @@ __global__ void __launch_bounds__(2 * kThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd_pp_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                  T* __restrict__ O, float* __restrict__ LSE, int BH, int kv_group, int N,
-                 float c /* score_coef(scale) */) {
+                 float c /* score_coef(scale) */, int fsplit, float* __restrict__ opart,
+                 float* __restrict__ lpart) {
   static_assert(sizeof(T) == 2, "bf16 only");
   using E = Elem<T>;
   using frag = typename E::frag;
@@ -358,8 +359,13 @@ fa_fwd_pp_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
   const int G = w >> 2, wg = w & 3;
   const int nqb = (N + BR - 1) / BR;
-  const BlockCoord bc = map_block(blockIdx.x, nqb, BH, CAUSAL, true);
-  const int bh = bc.bh, q0 = bc.blk * BR;
+  // With fsplit > 1 each query block's key tiles are cut into fsplit runs
+  // of equal length, one per work-group (the runs of one block count as
+  // separate heads in the block order); a run writes its normalised O and
+  // its LSE in fp32 (opart [fsplit][BH * N][D], lpart [fsplit][BH * N]) and a
+  // combine kernel merges the runs.
+  const BlockCoord bc = map_block(blockIdx.x, nqb, BH * fsplit, CAUSAL, true);
+  const int bh = bc.bh / fsplit, run = bc.bh - bh * fsplit, q0 = bc.blk * BR;
   const size_t head = (size_t)bh * N * D;
   const size_t kvhead = (size_t)(bh / kv_group) * N * D;    // shared key/value head
   const T* Kh = K + kvhead;
@@ -379,13 +385,17 @@ fa_fwd_pp_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
     for (int t = 0; t < NT; ++t) negate(qf[t]);
   }
 
-  // Tiles of the work-group, and of this wave's group (causal: the first
-  // group's rows end 128 keys earlier).
-  const int ntiles = ((CAUSAL ? min(N, q0 + BR) : N) + BC - 1) / BC;
-  const int gtiles = ((CAUSAL ? min(N, q0 + 128 * (G + 1)) : N) + BC - 1) / BC;
+  // Tiles of the work-group's run [tb, tb + ntiles), and the end of this
+  // wave's group's tiles within it (causal: the first group's rows end 128
+  // keys earlier); the walk below counts tiles from tb.
+  const int ntiles_all = ((CAUSAL ? min(N, q0 + BR) : N) + BC - 1) / BC;
+  const int tb = (int)((long long)run * ntiles_all / fsplit);
+  const int ntiles = (int)((long long)(run + 1) * ntiles_all / fsplit) - tb;
+  const int gtiles = max(0, min(((CAUSAL ? min(N, q0 + 128 * (G + 1)) : N) + BC - 1) / BC,
+                                tb + ntiles) - tb);
 
   auto stage = [&](int t, auto sl) {
-    const int kv0 = t * BC;
+    const int kv0 = (tb + t) * BC;
     const uint32_t left = (uint32_t)(N - kv0) * RB;
     unsigned char* base = pick3(sl, slot0, slot1, slot2);
     stage_tile<T, D, BC, 8>(make_rsrc(Kh + (size_t)kv0 * D, left), base, w, lane);
@@ -457,7 +467,7 @@ fa_fwd_pp_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   auto softmax = [&](int t, auto vs) {
     if (t < 0 || t >= gtiles) return;
     read_v(vs);
-    const int kv0 = t * BC;
+    const int kv0 = (tb + t) * BC;
     if ((kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > row0)) {
       const int lim = (CAUSAL ? min(N, qrow + 1) : N) - kv0 - 4 * g;
 #pragma unroll
@@ -518,7 +528,7 @@ fa_fwd_pp_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
     __syncthreads();
   };
 
-  stage(0, IntTag<0>{});
+  if (ntiles > 0) stage(0, IntTag<0>{});
   wait_global_loads();
   __syncthreads();
   for (int s = 0; s <= ntiles;) {
@@ -531,9 +541,23 @@ fa_fwd_pp_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
 
   const float l_tot = sum_xor32(l_run);
   const float inv = l_tot != 0.f ? 1.0f / l_tot : 0.f;
-  if (qrow < N && g == 0)
-    LSE[(size_t)bh * N + qrow] =
-        l_tot != 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : neg_inf();
+  const float lse = l_tot != 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : neg_inf();
+  if (fsplit > 1) {
+    if (qrow < N) {
+      const size_t r = ((size_t)run * BH + bh) * N + qrow;
+      if (g == 0) lpart[r] = lse;
+      float* po = opart + r * D;
+#pragma unroll
+      for (int b = 0; b < ND; ++b)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          *reinterpret_cast<f32x4*>(po + 32 * b + 8 * a + 4 * g) =
+              f32x4{oacc[b][4 * a], oacc[b][4 * a + 1], oacc[b][4 * a + 2],
+                    oacc[b][4 * a + 3]} * inv;
+    }
+    return;
+  }
+  if (qrow < N && g == 0) LSE[(size_t)bh * N + qrow] = lse;
   // O through LDS (fa_rows.hpp, unpadded): group G's 128 rows in slot G.
   static_assert(128 * D * (int)sizeof(T) <= 2 * TB, "O rows must fit a ring slot");
   __syncthreads();                                    // every wave is done with the ring
@@ -551,13 +575,58 @@ fa_fwd_pp_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
                                          tid & (kThreads - 1));
 }
 
+// Merge of the runs of a split forward, per row, in run order: with M the
+// largest run LSE and w_r = e^(LSE_r - M), LSE = M + ln sum_r w_r and
+// O = sum_r w_r O_r / sum_r w_r (the two-part merge rule of the reading
+// guide's "Artımsal Softmax Takibi", each run's statistics carried as its
+// LSE).  32 lanes per row (4 columns each at d = 128, 2 at d = 64).
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads)
+fa_fwd_combine_kernel(const float* __restrict__ opart, const float* __restrict__ lpart,
+                      T* __restrict__ O, float* __restrict__ LSE, int rows, int fsplit) {
+  constexpr int CPL = D / 32;              // columns per lane
+  const int row = blockIdx.x * (kThreads / 32) + (threadIdx.x >> 5);
+  const int c0 = (threadIdx.x & 31) * CPL;
+  if (row >= rows) return;
+  float M = neg_inf();
+  for (int r = 0; r < fsplit; ++r) M = fmaxf(M, lpart[(size_t)r * rows + row]);
+  float acc[CPL] = {};
+  float wsum = 0.f;
+  if (M != neg_inf()) {
+    for (int r = 0; r < fsplit; ++r) {
+      const float lr = lpart[(size_t)r * rows + row];
+      const float wr = __builtin_amdgcn_exp2f((lr - M) * kLog2e);
+      const float* po = opart + ((size_t)r * rows + row) * D + c0;
+      wsum += wr;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) acc[e] = fmaf(wr, po[e], acc[e]);
+    }
+  }
+  const float inv = wsum != 0.f ? 1.0f / wsum : 0.f;
+  T* out = O + (size_t)row * D + c0;
+#pragma unroll
+  for (int e = 0; e < CPL; e += 2) {
+    out[e] = (T)(acc[e] * inv);
+    out[e + 1] = (T)(acc[e + 1] * inv);
+  }
+  if ((threadIdx.x & 31) == 0)
+    LSE[row] = wsum != 0.f ? M + __builtin_amdgcn_logf(wsum) * kLn2 : neg_inf();
+}
+
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_fwd_pp(const FwdArgs& a) {
   const int nqb = (a.N + 255) / 256;
-  hipLaunchKernelGGL((fa_fwd_pp_kernel<T, D, CAUSAL>), dim3(nqb * a.BH), dim3(2 * kThreads), 0,
-                     a.stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                     static_cast<const T*>(a.v), static_cast<T*>(a.o), a.lse, a.BH, a.G, a.N,
-                     score_coef(a.scale));
+  hipLaunchKernelGGL((fa_fwd_pp_kernel<T, D, CAUSAL>), dim3(nqb * a.BH * a.fsplit),
+                     dim3(2 * kThreads), 0, a.stream, static_cast<const T*>(a.q),
+                     static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                     static_cast<T*>(a.o), a.lse, a.BH, a.G, a.N, score_coef(a.scale), a.fsplit,
+                     a.opart, a.lpart);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.fsplit == 1) return e;
+  const int rows = a.BH * a.N;
+  hipLaunchKernelGGL((fa_fwd_combine_kernel<T, D>), dim3((rows + kThreads / 32 - 1) / (kThreads / 32)),
+                     dim3(kThreads), 0, a.stream, a.opart, a.lpart, static_cast<T*>(a.o), a.lse,
+                     rows, a.fsplit);
   return hipGetLastError();
 }
 

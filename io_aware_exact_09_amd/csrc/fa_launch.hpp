@@ -29,6 +29,10 @@ struct FwdArgs {
   bool causal, bf16;
   Dropout drop;
   hipStream_t stream;
+  int fsplit = 1;          // work-groups sharing one query block's key tiles (ping-pong
+                           // forward only)
+  float* opart = nullptr;  // fp32 run outputs [fsplit][BH * N][d] (fsplit > 1)
+  float* lpart = nullptr;  // fp32 run LSE [fsplit][BH * N] (fsplit > 1)
 };
 
 struct BwdArgs {

@@ -60,6 +60,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp]
         lib.fa_fwd.restype = i
         lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
+        lib.fa_fwd_workspace_bytes.argtypes = [i, i, i, i]
+        lib.fa_fwd_workspace_bytes.restype = sz
+        lib.fa_fwd_ws.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp]
+        lib.fa_fwd_ws.restype = i
         lib.fa_bwd_splits.argtypes = [i, i, i, i, i, i, ctypes.POINTER(ctypes.c_int),
                                       ctypes.POINTER(ctypes.c_int)]
         lib.fa_bwd_splits.restype = ctypes.c_int
@@ -195,6 +199,32 @@ def fa_fwd(q, k, v, o, lse, scale: float, causal: bool = False, block_mask=None,
     st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
                     int(bool(causal)), _ptr(block_mask), _dtype_code(q), _stream(stream))
     _check(st, "fa_fwd")
+
+
+def fa_fwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(load_library().fa_fwd_workspace_bytes(B, H, N, d))
+
+
+def fa_fwd_ws(q, k, v, o, lse, scale: float, causal: bool = False, block_mask=None,
+              workspace=None, stream=None) -> None:
+    """fa_fwd with a workspace, which lets shapes that fill few compute units
+    run split (``workspace``: a device tensor of fa_fwd_workspace_bytes(B, H,
+    N, d) bytes, allocated here if None; None and a size of 0: plain fa_fwd)."""
+    lib = load_library()
+    _check_tensors(q, dict(q=q, k=k, v=v, o=o, lse=lse))
+    B, H, N, d = q.shape
+    if block_mask is not None:
+        _check_tensors(q, dict(block_mask=block_mask))
+        if block_mask.dtype != torch.uint8:
+            raise TypeError("block_mask must be uint8")
+    if workspace is None:
+        need = fa_fwd_workspace_bytes(B, H, N, d)
+        workspace = _scratch(need, q, stream) if need else None
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.fa_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                       int(bool(causal)), _ptr(block_mask), _dtype_code(q), _ptr(workspace),
+                       wbytes, _stream(stream))
+    _check(st, "fa_fwd_ws")
 
 
 def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = False,
@@ -434,10 +464,11 @@ def decode(q, k, v, scale: float, seqlens=None, causal: bool = False, num_splits
 
 
 def forward(q, k, v, scale: float, causal: bool = False, block_mask=None, stream=None):
+    """O, LSE through fa_fwd_ws (so shapes that fill few compute units run split)."""
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     _mark(stream, o, lse)
-    fa_fwd(q, k, v, o, lse, scale, causal, block_mask, stream)
+    fa_fwd_ws(q, k, v, o, lse, scale, causal, block_mask, None, stream)
     return o, lse
 
 

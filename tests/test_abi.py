@@ -34,7 +34,8 @@ def test_header_symbols_are_exported(lib):
                           "fa_fwd_dropout", "fa_bwd_dropout", "fa_decode", "fa_fwd_gqa",
                           "fa_bwd_gqa", "fa_fwd_fp8", "fa_bwd_gqa_workspace_bytes",
                           "fa_decode_num_splits", "fa_decode_workspace_bytes",
-                          "fa_bwd_static", "fa_bwd_dq_and_d", "fa_bwd_splits"}
+                          "fa_bwd_static", "fa_bwd_dq_and_d", "fa_bwd_splits",
+                          "fa_fwd_ws", "fa_fwd_workspace_bytes"}
     out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -70,6 +71,18 @@ def test_bwd_splits(lib):
         fa.fa_bwd_splits(1, 6, 4, 100, 64, "bf16")
     st = lib.fa_bwd_splits(1, 1, 1, 128, 64, 0, None, None)
     assert st == 1      # FA_ERR_NULL
+
+
+def test_fwd_workspace_bytes(lib):
+    # one head of 16K rows: 64 blocks of 256 rows -> 8 runs; O, then LSE, in fp32
+    rows = 16384
+    assert fa.fa_fwd_workspace_bytes(1, 1, 16384, 128) == 8 * rows * 128 * 4 + 8 * rows * 4
+    # enough blocks, d = 64 (the four-wave forward), or too few key tiles: no split
+    assert fa.fa_fwd_workspace_bytes(2, 16, 4096, 128) == 0
+    assert fa.fa_fwd_workspace_bytes(1, 1, 16384, 64) == 0
+    assert fa.fa_fwd_workspace_bytes(1, 1, 1000, 128) == 2 * 1000 * 128 * 4 + 2 * 1000 * 4
+    assert fa.fa_fwd_workspace_bytes(1, 1, 900, 128) == 0
+    assert fa.fa_fwd_workspace_bytes(0, 1, 16384, 128) == 0
 
 
 def test_workspace_bytes(lib):

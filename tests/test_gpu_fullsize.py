@@ -111,13 +111,20 @@ def test_workload_whole_tensors(name):
 
 def test_verylong_shard_rows():
     """One GPU's share of verylong split by heads (B=1, H=1, N=16384): the
-    backward runs split (dK/dV 4 runs of query tiles, dQ 8 runs of key
-    tiles); 1024 query and 1024 key rows against the row oracle."""
+    forward runs split (8 runs of key tiles per 256-row block), the backward
+    too (dK/dV 4 runs of query tiles, dQ 8 runs of key tiles); 1024 query
+    and 1024 key rows against the row oracle."""
+    assert fa.fa_fwd_workspace_bytes(1, 1, 16384, 128) > 0
     w = W.WORKLOADS["verylong_shard"]
     assert fa.fa_bwd_splits(w.B, w.H, w.H, w.N, w.d, "bf16") == (4, 8)
     x = W.make_inputs(w)
     _say(f"workload verylong_shard: B={w.B} H={w.H} N={w.N} d={w.d}")
-    got = _run_workload(w, x)
+    # the forward in 8 runs of key tiles per 256-row block (fa_fwd_ws)
+    q, k, v, do = (upload(x[n], w.dtype) for n in ("q", "k", "v", "do"))
+    o, lse = fa.forward(q, k, v, w.scale, w.causal)
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, w.scale, w.causal)
+    torch.cuda.synchronize()
+    got = {"O": o, "LSE": lse, "dQ": dq, "dK": dk, "dV": dv}
     rng = np.random.default_rng(29)
     fixed = np.array([0, 1, 63, 64, 127, 128, 255, 256, w.N // 2, w.N - 129, w.N - 128,
                       w.N - 1])

@@ -115,6 +115,38 @@ def test_split_backward_against_oracle(B, H, N, d, causal, mk):
         tol_check(n, f64(a), f64(b), "bf16")
 
 
+FWD_SPLIT = [
+    # (B, H, N, causal): bf16, d = 128, runs of key tiles per 256-row block
+    (1, 1, 4096, True), (1, 2, 3000, False), (1, 1, 1000, True), (2, 1, 2049, True),
+]
+
+
+@pytest.mark.parametrize("B,H,N,causal", FWD_SPLIT,
+                         ids=[f"B{a}-H{b}-N{c}-{'causal' if e else 'dense'}"
+                              for a, b, c, e in FWD_SPLIT])
+def test_split_forward_against_oracle(B, H, N, causal):
+    """fa_fwd_ws with its workspace (runs of key tiles, merged per row)
+    against the full oracle and against fa_fwd, which never splits."""
+    d = 128
+    need = fa.fa_fwd_workspace_bytes(B, H, N, d)
+    _say(f"case B={B} H={H} N={N} causal={causal}: workspace {need} bytes")
+    assert need > 0
+    inp = W.random_inputs(B, H, N, d, "bf16", seed=3 * N + B)
+    scale = 1.0 / math.sqrt(d)
+    q, k, v = (upload(inp[n], "bf16") for n in ("q", "k", "v"))
+    o, lse = torch.empty_like(q), torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    o1, lse1 = torch.empty_like(o), torch.empty_like(lse)
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    fa.fa_fwd_ws(q, k, v, o, lse, scale, causal, None, ws)
+    fa.fa_fwd(q, k, v, o1, lse1, scale, causal, None)
+    torch.cuda.synchronize()
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
+    ro, rl = oracle.forward(inp["q"], inp["k"], inp["v"], scale, causal, None)
+    check_all({"O": f64(o), "LSE": f64(lse)}, {"O": ro, "LSE": rl}, "bf16", "split forward")
+    check_all({"O": f64(o), "LSE": f64(lse)}, {"O": f64(o1), "LSE": f64(lse1)}, "bf16",
+              "split vs fa_fwd")
+
+
 def test_fully_masked_rows():
     """A mask that drops a diagonal tile under causal masking leaves query
     rows with no key: O = 0, LSE = -inf, dQ = 0, nothing NaN."""
