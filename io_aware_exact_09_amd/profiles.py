@@ -34,9 +34,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 PROFILES = os.path.join(ROOT, "profiles")
 
-KERNELS = ("fa_fwd_kernel", "fa_fwd_pp_kernel", "fa_bwd_delta_kernel", "fa_bwd_dkdv_kernel",
-           "fa_bwd_dkdv_reduce_kernel",
-           "fa_bwd_dq_kernel", "fa_decode_split_kernel", "fa_decode_combine_kernel",
+KERNELS = ("fa_fwd_kernel", "fa_fwd_pp_kernel", "fa_fwd_combine_kernel", "fa_bwd_delta_kernel",
+           "fa_bwd_dkdv_kernel", "fa_bwd_dkdv_reduce_kernel", "fa_bwd_dq_kernel",
+           "fa_bwd_dq_reduce_kernel", "fa_decode_split_kernel", "fa_decode_combine_kernel",
            "fa_fwd_fp8_kernel")
 
 # Device sources of each kernel family (host-side files such as fa_api.cpp
