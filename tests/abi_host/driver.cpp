@@ -239,9 +239,50 @@ static void status_cases() {
   EXPECT(std::strcmp(fa_status_str((fa_status)-1), "unknown status") == 0);
 }
 
+// Shapes whose blocks fill few compute units (one head of 16K rows) run
+// split: the forward's runs land in its workspace (O, then LSE), the
+// backward's partials after D (dK/dV, then dQ); smaller workspaces run unsplit.
+static void split_cases() {
+  const int N = 16384;
+  const unsigned long long orun = 8ull * N * 128 * 4;
+  const size_t fneed = fa_fwd_workspace_bytes(1, 1, N, 128);
+  EXPECT(fneed == orun + 8ull * N * 4);
+  auto fws = [&](void* ws, size_t wsb, fa_dtype dt = FA_BF16, void* o = P(3)) {
+    return fa_fwd_ws(P(0), P(1), P(2), o, F(4), 1, 1, N, 128, 0.1f, 1, nullptr, dt, ws, wsb,
+                     nullptr);
+  };
+  ACCEPT(1, fws(P(9), fneed));
+  EXPECT(fa::g_fwd.fsplit == 8 && fa::g_fwd.opart == F(9) && fa::g_fwd.lpart == F(9, orun));
+  ACCEPT(1, fws(P(9), fneed - 1));
+  EXPECT(fa::g_fwd.fsplit == 1 && fa::g_fwd.opart == nullptr);
+  ACCEPT(1, fws(nullptr, 0));
+  EXPECT(fa::g_fwd.fsplit == 1);
+  ACCEPT(1, fws(P(9), fneed, FA_FP32));
+  EXPECT(fa::g_fwd.fsplit == 1);
+  REJECT(FA_ERR_WORKSPACE, fws(nullptr, 16));
+  REJECT(FA_ERR_WORKSPACE, fws(P(9, 8), fneed));
+  REJECT(FA_ERR_ALIAS, fws(P(3), fneed));
+  REJECT(FA_ERR_ALIAS, fws(P(9), fneed, FA_BF16, P(9, orun)));
+  EXPECT(fa_fwd_workspace_bytes(2, 16, 4096, 128) == 0);
+
+  int kv = 0, q = 0;
+  EXPECT(fa_bwd_splits(1, 1, 1, N, 128, FA_BF16, &kv, &q) == FA_OK && kv == 4 && q == 8);
+  EXPECT(fa_bwd_splits(1, 1, 1, N, 128, FA_BF16, nullptr, &q) == FA_ERR_NULL);
+  EXPECT(fa_bwd_splits(1, 6, 4, N, 128, FA_BF16, &kv, &q) == FA_ERR_SHAPE);
+  const unsigned long long d_bytes = 4ull * N, kv_bytes = 2ull * 4 * N * 128 * 4;
+  const size_t bneed = fa_bwd_workspace_bytes(1, 1, N, 128);
+  EXPECT(bneed == d_bytes + kv_bytes + 8ull * N * 128 * 4);
+  ACCEPT(2, bwd(1, 1, N, 128, 0.1f, FA_BF16, P(9), bneed));
+  EXPECT(fa::g_bwd.gsplit == 4 && fa::g_bwd.part == F(9, d_bytes));
+  EXPECT(fa::g_dq.ksplit == 8 && fa::g_dq.qpart == F(9, d_bytes + kv_bytes));
+  ACCEPT(2, bwd(1, 1, N, 128, 0.1f, FA_BF16, P(9), d_bytes));
+  EXPECT(fa::g_bwd.gsplit == 1 && fa::g_dq.ksplit == 1 && fa::g_dq.qpart == nullptr);
+}
+
 int main() {
   forward_cases();
   backward_cases();
+  split_cases();
   static_scratch_cases();
   fp8_cases();
   decode_cases();

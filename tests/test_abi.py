@@ -103,6 +103,24 @@ def fwd(lib, q=p(0), k=p(1), v=p(2), o=p(3), lse=p(4), B=1, H=2, N=128, d=64, sc
     return lib.fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, mask, dtype, None)
 
 
+def fwd_ws(lib, q=p(0), k=p(1), v=p(2), o=p(3), lse=p(4), B=1, H=2, N=128, d=64, scale=0.125,
+           causal=0, mask=None, dtype=BF16, ws=p(9), wsb=1 << 20):
+    return lib.fa_fwd_ws(q, k, v, o, lse, B, H, N, d, scale, causal, mask, dtype, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(B=0), 2), (dict(d=96), 3), (dict(dtype=7), 4),
+    (dict(o=p(3, 4)), 5), (dict(scale=float("nan")), 8), (dict(o=p(0, 64)), 9),
+    (dict(ws=None), 6),            # NULL with a nonzero size
+    (dict(ws=p(9, 4)), 6),         # not 16-byte aligned
+    (dict(ws=p(3)), 9),            # overlaps O
+    (dict(ws=p(1)), 9),            # overlaps K
+    (dict(ws=p(4, 256)), 9),       # overlaps LSE
+])
+def test_fwd_ws_validation(lib, kw, code):
+    assert fwd_ws(lib, **kw) == code
+
+
 def bwd(lib, q=p(0), k=p(1), v=p(2), o=p(3), do=p(4), lse=p(5), dq=p(6), dk=p(7), dv=p(8),
         B=1, H=2, N=128, d=64, scale=0.125, causal=0, mask=None, dtype=BF16, ws=p(9),
         wsb=1 << 20):
