@@ -115,18 +115,19 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
 
 /*
  * fa_fwd_workspace_bytes / fa_fwd_ws -- the forward with an optional
- * workspace.  For bf16 at d = 128 without a block mask, a shape with fewer
- * than 256 blocks of 256 query rows (B * H * ceil(N/256) < 256, e.g. one
- * head of a long sequence) leaves most of the GPU idle while its last block
- * walks every key; given a workspace of at least fa_fwd_workspace_bytes
- * bytes, fa_fwd_ws cuts each block's 64-key tiles into runs (at most 8, at
- * least 8 tiles each), one work-group per run, each writing its normalised
- * O and its LSE in fp32 to the workspace (O: runs * B*H*N*d * 4 bytes, then
- * LSE: runs * B*H*N * 4 bytes), and a second kernel merges the runs per row
- * in run order with the two-part rule ([FA-guide] "Artımsal Softmax
- * Takibi"): deterministic, equal to fa_fwd's result up to rounding.
- * fa_fwd_workspace_bytes returns 0 when no split applies; then, and with a
- * smaller or NULL workspace (workspace_bytes 0), fa_fwd_ws is fa_fwd.
+ * workspace.  In bf16, a shape with fewer than 256 query blocks (of 256 rows
+ * at d = 128 without a block mask, else of 128 rows; e.g. one head of a long
+ * sequence) leaves most of the GPU idle while its last block walks every
+ * key; given a workspace of at least fa_fwd_workspace_bytes bytes,
+ * fa_fwd_ws cuts each block's 64-key tiles into runs (at most 8, at least 8
+ * tiles each), one work-group per run, each writing its normalised O and its
+ * LSE in fp32 to the workspace (O: runs * B*H*N*d * 4 bytes, then LSE:
+ * runs * B*H*N * 4 bytes), and a second kernel merges the runs per row in
+ * run order with the two-part rule ([FA-guide] "Artımsal Softmax Takibi"):
+ * deterministic, equal to fa_fwd's result up to rounding.
+ * fa_fwd_workspace_bytes (the larger of the unmasked and block-masked
+ * plans) returns 0 when no split applies; then, and with a smaller or NULL
+ * workspace (workspace_bytes 0), fa_fwd_ws is fa_fwd.
  * The workspace is caller-owned device memory, 16-byte aligned, not
  * overlapping any argument (FA_ERR_WORKSPACE / FA_ERR_ALIGN / FA_ERR_ALIAS);
  * other arguments and errors as for fa_fwd.

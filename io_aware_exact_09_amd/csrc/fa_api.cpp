@@ -189,11 +189,13 @@ BwdPlan bwd_plan(const Shape& s, int Hkv, bool seq_splits) {
   return p;
 }
 
-// Forward split (the ping-pong kernel: bf16, d = 128, no block mask, no
-// dropout): with fewer than 256 blocks of 256 query rows, each block's key
-// tiles are cut into runs (at most 8, at least 8 tiles of 64 keys each),
-// aiming at 512 work-groups; the runs' fp32 O and LSE go to the workspace
-// (O first, then LSE) and a combine kernel merges them in run order.
+// Forward split (bf16, no dropout): with fewer than 256 query blocks (of 256
+// rows in the ping-pong kernel, d = 128 without a block mask; of 128 rows in
+// the four-wave kernel otherwise), each block's key tiles are cut into runs
+// (at most 8, at least 8 tiles of 64 keys each), aiming at 512 work-groups
+// for the ping-pong kernel (one per CU) and 1024 for the four-wave kernel
+// (two per CU); the runs' fp32 O and LSE go to the workspace (O first, then
+// LSE) and a combine kernel merges them in run order.
 struct FwdPlan {
   int runs = 1;
   size_t lse_off = 0, bytes = 0;   // bytes = 0: no split
@@ -201,8 +203,11 @@ struct FwdPlan {
 
 FwdPlan fwd_plan(const Shape& s, bool masked, bool dropout) {
   FwdPlan p;
-  if (s.dtype != FA_BF16 || s.d != 128 || masked || dropout) return p;
-  p.runs = run_split((long long)s.B * s.H * ((s.N + 255) / 256), 2LL * kCUs, (s.N + 63) / 64, 8);
+  if (s.dtype != FA_BF16 || dropout) return p;
+  const bool pp = s.d == 128 && !masked;
+  const int br = pp ? 256 : 128;
+  p.runs = run_split((long long)s.B * s.H * ((s.N + br - 1) / br), (pp ? 2LL : 4LL) * kCUs,
+                     (s.N + 63) / 64, 8);
   if (p.runs == 1) return p;
   const size_t rows = (size_t)s.B * s.H * s.N;
   p.lse_off = (size_t)p.runs * rows * s.d * 4;
@@ -222,7 +227,7 @@ FA_EXPORT fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O,
 FA_EXPORT size_t fa_fwd_workspace_bytes(int B, int H, int N, int d) {
   const Shape s{B, H, N, d, FA_BF16};
   if (check_shape(s, 1.0f) != FA_OK) return 0;
-  return fwd_plan(s, false, false).bytes;
+  return std::max(fwd_plan(s, false, false).bytes, fwd_plan(s, true, false).bytes);
 }
 
 FA_EXPORT fa_status fa_fwd_ws(const void* Q, const void* K, const void* V, void* O, float* LSE,

@@ -45,7 +45,7 @@ __attribute__((amdgpu_waves_per_eu(Occupancy<T, D>::fwd, Occupancy<T, D>::fwd)))
 fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
               T* __restrict__ O, float* __restrict__ LSE, const uint8_t* __restrict__ mask,
               int BH, int kv_group, int N, int T_tiles, float c /* score_coef(scale) */,
-              DropParams dp) {
+              DropParams dp, int fsplit, float* __restrict__ opart, float* __restrict__ lpart) {
   using E = Elem<T>;
   using frag = typename E::frag;
   using Cfg = FwdCfg<T>;
@@ -63,8 +63,9 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
   const int nqb = (N + BR - 1) / BR;
-  const BlockCoord bc = map_block(blockIdx.x, nqb, BH, CAUSAL, true);
-  const int bh = bc.bh, q0 = bc.blk * BR;
+  // fsplit > 1: runs of key tiles per query block, as in the ping-pong kernel.
+  const BlockCoord bc = map_block(blockIdx.x, nqb, BH * fsplit, CAUSAL, true);
+  const int bh = bc.bh / fsplit, run = bc.bh - bh * fsplit, q0 = bc.blk * BR;
   const size_t head = (size_t)bh * N * D;
   const size_t kvhead = (size_t)(bh / kv_group) * N * D;    // shared key/value head
   const T* Kh = K + kvhead;
@@ -92,7 +93,9 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   }
 
   const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
-  const int ntiles = (kv_end + BC - 1) / BC;
+  const int ntiles_all = (kv_end + BC - 1) / BC;
+  const int jbeg = (int)((long long)run * ntiles_all / fsplit);
+  const int ntiles = (int)((long long)(run + 1) * ntiles_all / fsplit);   // end of this run
   KeptTiles<BC> kept(MASKED ? mask + (size_t)(q0 / kMaskBlock) * T_tiles : nullptr, 1, T_tiles);
   auto next_kept = [&](int j) {
     if constexpr (MASKED) return kept.next(j, lane);
@@ -247,7 +250,7 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
 
   // Wait for kept tile j (buffer buf_tag), prefetch the next kept tile into
   // the other buffer, then run the tile.
-  int j = next_kept(0);
+  int j = next_kept(jbeg);
   bool first = true;
   auto step = [&](auto buf_tag) {
     wait_global_loads();             // this wave's part of tile j has landed
@@ -272,9 +275,23 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   // ---- epilogue ----------------------------------------------------------------
   const float l_tot = sum_xor32(l_run);
   const float inv = l_tot != 0.f ? (DROP ? dp.inv_keep : 1.0f) / l_tot : 0.f;
-  if (qrow < N && g == 0)
-    LSE[(size_t)bh * N + qrow] =
-        l_tot != 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : neg_inf();
+  const float lse = l_tot != 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : neg_inf();
+  if (fsplit > 1) {
+    if (qrow < N) {
+      const size_t r = ((size_t)run * BH + bh) * N + qrow;
+      if (g == 0) lpart[r] = lse;
+      float* po = opart + r * D;
+#pragma unroll
+      for (int b = 0; b < ND; ++b)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          *reinterpret_cast<f32x4*>(po + 32 * b + 8 * a + 4 * g) =
+              f32x4{oacc[b][4 * a], oacc[b][4 * a + 1], oacc[b][4 * a + 2],
+                    oacc[b][4 * a + 3]} * inv;
+    }
+    return;
+  }
+  if (qrow < N && g == 0) LSE[(size_t)bh * N + qrow] = lse;
   if constexpr (sizeof(T) == 2) {
     // O through LDS (fa_rows.hpp; padded rows would not fit).
     static_assert(BR * D * (int)sizeof(T) <= 2 * TB, "O rows must fit a staging array");
@@ -299,22 +316,27 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   }
 }
 
+template <typename T, int D>
+static hipError_t launch_fwd_combine(const FwdArgs& a);
+
 template <typename T, int D, bool CAUSAL, bool MASKED>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
   const int nqb = (a.N + FwdCfg<T>::BR - 1) / FwdCfg<T>::BR;
-  const dim3 grid(nqb * a.BH), block(kThreads);
+  const dim3 grid(nqb * a.BH * a.fsplit), block(kThreads);
   const DropParams dp{a.drop.key0, a.drop.key1, a.drop.thresh, a.drop.inv_keep};
   if (a.drop.on)
     hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, MASKED, true>), grid, block, 0, a.stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), static_cast<T*>(a.o), a.lse, a.mask, a.BH,
-                       a.G, a.N, a.T, score_coef(a.scale), dp);
+                       a.G, a.N, a.T, score_coef(a.scale), dp, a.fsplit, a.opart, a.lpart);
   else
     hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, MASKED, false>), grid, block, 0, a.stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), static_cast<T*>(a.o), a.lse, a.mask, a.BH,
-                       a.G, a.N, a.T, score_coef(a.scale), dp);
-  return hipGetLastError();
+                       a.G, a.N, a.T, score_coef(a.scale), dp, a.fsplit, a.opart, a.lpart);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.fsplit == 1) return e;
+  return launch_fwd_combine<T, D>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -623,6 +645,11 @@ static hipError_t launch_fwd_pp(const FwdArgs& a) {
                      a.opart, a.lpart);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.fsplit == 1) return e;
+  return launch_fwd_combine<T, D>(a);
+}
+
+template <typename T, int D>
+static hipError_t launch_fwd_combine(const FwdArgs& a) {
   const int rows = a.BH * a.N;
   hipLaunchKernelGGL((fa_fwd_combine_kernel<T, D>), dim3((rows + kThreads / 32 - 1) / (kThreads / 32)),
                      dim3(kThreads), 0, a.stream, a.opart, a.lpart, static_cast<T*>(a.o), a.lse,

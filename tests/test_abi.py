@@ -77,9 +77,11 @@ def test_fwd_workspace_bytes(lib):
     # one head of 16K rows: 64 blocks of 256 rows -> 8 runs; O, then LSE, in fp32
     rows = 16384
     assert fa.fa_fwd_workspace_bytes(1, 1, 16384, 128) == 8 * rows * 128 * 4 + 8 * rows * 4
-    # enough blocks, d = 64 (the four-wave forward), or too few key tiles: no split
+    # d = 64 (the four-wave forward, 128-row blocks): 128 blocks -> 8 runs
+    assert fa.fa_fwd_workspace_bytes(1, 1, 16384, 64) == 8 * rows * 64 * 4 + 8 * rows * 4
+    # enough blocks, or too few key tiles: no split
     assert fa.fa_fwd_workspace_bytes(2, 16, 4096, 128) == 0
-    assert fa.fa_fwd_workspace_bytes(1, 1, 16384, 64) == 0
+    assert fa.fa_fwd_workspace_bytes(4, 8, 8192, 64) == 0
     assert fa.fa_fwd_workspace_bytes(1, 1, 1000, 128) == 2 * 1000 * 128 * 4 + 2 * 1000 * 4
     assert fa.fa_fwd_workspace_bytes(1, 1, 900, 128) == 0
     assert fa.fa_fwd_workspace_bytes(0, 1, 16384, 128) == 0

@@ -116,32 +116,36 @@ def test_split_backward_against_oracle(B, H, N, d, causal, mk):
 
 
 FWD_SPLIT = [
-    # (B, H, N, causal): bf16, d = 128, runs of key tiles per 256-row block
-    (1, 1, 4096, True), (1, 2, 3000, False), (1, 1, 1000, True), (2, 1, 2049, True),
+    # (B, H, N, d, causal, mask-kind): bf16, runs of key tiles per query block
+    # (the ping-pong kernel at d = 128 without a mask, else the four-wave one)
+    (1, 1, 4096, 128, True, None), (1, 2, 3000, 128, False, None), (1, 1, 1000, 128, True, None),
+    (2, 1, 2049, 128, True, None), (1, 1, 4096, 64, True, None), (1, 2, 2048, 64, False, "rand"),
+    (1, 1, 3000, 128, True, "rand"),
 ]
 
 
-@pytest.mark.parametrize("B,H,N,causal", FWD_SPLIT,
-                         ids=[f"B{a}-H{b}-N{c}-{'causal' if e else 'dense'}"
-                              for a, b, c, e in FWD_SPLIT])
-def test_split_forward_against_oracle(B, H, N, causal):
+@pytest.mark.parametrize("B,H,N,d,causal,mk", FWD_SPLIT,
+                         ids=[f"B{a}-H{b}-N{c}-d{e}-{'causal' if f else 'dense'}-{g or 'nomask'}"
+                              for a, b, c, e, f, g in FWD_SPLIT])
+def test_split_forward_against_oracle(B, H, N, d, causal, mk):
     """fa_fwd_ws with its workspace (runs of key tiles, merged per row)
     against the full oracle and against fa_fwd, which never splits."""
-    d = 128
     need = fa.fa_fwd_workspace_bytes(B, H, N, d)
-    _say(f"case B={B} H={H} N={N} causal={causal}: workspace {need} bytes")
+    _say(f"case B={B} H={H} N={N} d={d} causal={causal} mask={mk}: workspace {need} bytes")
     assert need > 0
-    inp = W.random_inputs(B, H, N, d, "bf16", seed=3 * N + B)
+    inp = W.random_inputs(B, H, N, d, "bf16", seed=3 * N + B + d)
+    mask = W.random_block_mask(N, 0.6, seed=N + 1) if mk == "rand" else None
     scale = 1.0 / math.sqrt(d)
     q, k, v = (upload(inp[n], "bf16") for n in ("q", "k", "v"))
+    m = upload_mask(mask)
     o, lse = torch.empty_like(q), torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     o1, lse1 = torch.empty_like(o), torch.empty_like(lse)
     ws = torch.empty(need, dtype=torch.uint8, device=q.device)
-    fa.fa_fwd_ws(q, k, v, o, lse, scale, causal, None, ws)
-    fa.fa_fwd(q, k, v, o1, lse1, scale, causal, None)
+    fa.fa_fwd_ws(q, k, v, o, lse, scale, causal, m, ws)
+    fa.fa_fwd(q, k, v, o1, lse1, scale, causal, m)
     torch.cuda.synchronize()
     f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
-    ro, rl = oracle.forward(inp["q"], inp["k"], inp["v"], scale, causal, None)
+    ro, rl = oracle.forward(inp["q"], inp["k"], inp["v"], scale, causal, mask)
     check_all({"O": f64(o), "LSE": f64(lse)}, {"O": ro, "LSE": rl}, "bf16", "split forward")
     check_all({"O": f64(o), "LSE": f64(lse)}, {"O": f64(o1), "LSE": f64(lse1)}, "bf16",
               "split vs fa_fwd")
