@@ -693,7 +693,8 @@ struct DqCfg {
 
 template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP>
 __global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(Occupancy<T, D>::dq, Occupancy<T, D>::dq)))
+__attribute__((amdgpu_waves_per_eu(Occupancy<T, D, CAUSAL, MASKED, DROP>::dq,
+                                   Occupancy<T, D, CAUSAL, MASKED, DROP>::dq)))
 fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                  const T* __restrict__ dO, const T* __restrict__ O, const float* __restrict__ LSE,
                  float* __restrict__ delta, T* __restrict__ dQ,

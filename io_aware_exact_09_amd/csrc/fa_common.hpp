@@ -516,11 +516,18 @@ struct KeptTiles {
 
 // Waves per SIMD each kernel is compiled for (two waves let one wave's
 // softmax arithmetic overlap the other's matrix work; the fp32 path at
-// d = 128 needs the full register file of one wave).
-template <typename T, int D>
+// d = 128 needs the full register file of one wave).  bf16 at d = 64 fits a
+// third wave (168 VGPRs) in the forward and in the dQ pass without dropout,
+// except the plain non-causal forward, which would spill; a third
+// work-group per compute unit also lets every block of a 96-head, 1K-row
+// launch be resident at once.
+template <typename T, int D, bool CAUSAL = true, bool MASKED = false, bool DROP = false>
 struct Occupancy {
-  static constexpr int fwd = (sizeof(T) == 2 || D == 64) ? 2 : 1;
-  static constexpr int dq = (sizeof(T) == 2 || D == 64) ? 2 : 1;
+  static constexpr bool narrow = sizeof(T) == 2 && D == 64;
+  static constexpr int fwd = narrow && (CAUSAL || MASKED || DROP) ? 3
+                             : (sizeof(T) == 2 || D == 64)        ? 2
+                                                                  : 1;
+  static constexpr int dq = narrow && !DROP ? 3 : (sizeof(T) == 2 || D == 64) ? 2 : 1;
 };
 
 // ---------------------------------------------------------------------------

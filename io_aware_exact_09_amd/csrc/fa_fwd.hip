@@ -41,7 +41,8 @@ struct FwdCfg {
 
 template <typename T, int D, bool CAUSAL, bool MASKED, bool DROP>
 __global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(Occupancy<T, D>::fwd, Occupancy<T, D>::fwd)))
+__attribute__((amdgpu_waves_per_eu(Occupancy<T, D, CAUSAL, MASKED, DROP>::fwd,
+                                   Occupancy<T, D, CAUSAL, MASKED, DROP>::fwd)))
 fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
               T* __restrict__ O, float* __restrict__ LSE, const uint8_t* __restrict__ mask,
               int BH, int kv_group, int N, int T_tiles, float c /* score_coef(scale) */,

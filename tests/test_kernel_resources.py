@@ -42,6 +42,11 @@ OCCUPANCY = {
     # d = 64: two waves per SIMD (two work-groups per compute unit)
     ("fa_bwd_dkdv_kernel", ("bf16", 64, True, False, False)): 2,
     ("fa_bwd_dkdv_kernel", ("bf16", 64, False, True, False)): 2,
+    # d = 64 forward and dQ pass: three waves per SIMD
+    ("fa_fwd_kernel", ("bf16", 64, True, False, False)): 3,
+    ("fa_fwd_kernel", ("bf16", 64, False, True, False)): 3,
+    ("fa_bwd_dq_kernel", ("bf16", 64, True, False, False)): 3,
+    ("fa_bwd_dq_kernel", ("bf16", 64, False, True, False)): 3,
 }
 
 LDS_BYTES = 160 * 1024
