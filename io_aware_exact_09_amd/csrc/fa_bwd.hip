@@ -719,7 +719,8 @@ fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
   // of equal length, one per work-group, which write scale * their dQ
   // partial in fp32 (qpart, [ksplit][BH * N * D]) for a reduction kernel;
   // the runs of one block count as separate heads in the block order.
-  const BlockCoord bc = map_block(blockIdx.x, nqb, BH * ksplit, CAUSAL, true);
+  const BlockCoord bc = map_block(blockIdx.x, nqb, BH * ksplit, CAUSAL, true,
+                                  Occupancy<T, D, CAUSAL, MASKED, DROP>::dq);
   const int bh = bc.bh / ksplit, ksp = bc.bh - bh * ksplit, q0 = bc.blk * BR;
   const size_t head = (size_t)bh * N * D;
   const size_t kvhead = (size_t)(bh / kv_group) * N * D;    // shared key/value head

@@ -536,20 +536,32 @@ struct Occupancy {
 // Blocks are handed to the 8 XCDs round-robin by work-group id, and each XCD
 // has its own L2.  When the head count is a multiple of 8, head h is pinned to
 // XCD h % 8 so all blocks of a head share one L2 (they re-read the same K/V or
-// Q/dO tiles).  Within an XCD, blocks are ordered by decreasing work when
-// `heavy_first_desc` (causal query blocks: the last block has the most keys)
-// or `heavy_first_asc` (causal key blocks: the first block has the most
-// queries).
+// Q/dO tiles).  Under the causal mask, blocks are ordered by decreasing work
+// (`heavy_is_last`: causal query blocks, the last has the most keys; else
+// causal key blocks, the first has the most queries), so that work-groups
+// dispatched as compute units free up take the longest blocks first.
+//
+// When every work-group of the launch is resident at once (`wgs_per_cu`
+// work-groups per CU, 32 CUs per XCD), each CU's work is fixed at dispatch:
+// consecutive work-groups of an XCD land on consecutive CUs, so in that
+// order CU j would take blocks j, j + 32, j + 64, all heavy for small j and
+// all light for large j.  There every second round of 32 is reversed, and
+// each CU takes a heavy, a middle and a light block.
 // ---------------------------------------------------------------------------
 struct BlockCoord { int bh; int blk; };
 
 __device__ __forceinline__ BlockCoord map_block(int wg, int nblk, int BH, bool causal,
-                                                bool heavy_is_last) {
+                                                bool heavy_is_last, int wgs_per_cu = 0) {
   int rank, bh;
   if ((BH & 7) == 0) {
     const int xcd = wg & 7;
-    const int s = wg >> 3;
+    int s = wg >> 3;
     const int hpx = BH >> 3;          // heads per XCD
+    const int per = nblk * hpx;       // work-groups on this XCD
+    if (causal && per <= 32 * wgs_per_cu && ((s >> 5) & 1)) {
+      const int base = s & ~31;
+      s = base + min(32, per - base) - 1 - (s & 31);
+    }
     rank = s / hpx;
     bh = (s - rank * hpx) * 8 + xcd;
   } else {

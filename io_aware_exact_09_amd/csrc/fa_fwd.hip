@@ -65,7 +65,8 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
   const int nqb = (N + BR - 1) / BR;
   // fsplit > 1: runs of key tiles per query block, as in the ping-pong kernel.
-  const BlockCoord bc = map_block(blockIdx.x, nqb, BH * fsplit, CAUSAL, true);
+  const BlockCoord bc = map_block(blockIdx.x, nqb, BH * fsplit, CAUSAL, true,
+                                  Occupancy<T, D, CAUSAL, MASKED, DROP>::fwd);
   const int bh = bc.bh / fsplit, run = bc.bh - bh * fsplit, q0 = bc.blk * BR;
   const size_t head = (size_t)bh * N * D;
   const size_t kvhead = (size_t)(bh / kv_group) * N * D;    // shared key/value head
