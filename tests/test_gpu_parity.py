@@ -72,6 +72,25 @@ def test_small_against_full_oracle(N, d, dtype, causal, mk):
 
 
 # --------------------------------------------------------------------------
+# Causal launches whose work-groups all fit on the chip at once take their
+# blocks in serpentine order (every second round of 32 per XCD reversed).
+# 5 x 8 heads of 8 query blocks leave 40 work-groups per XCD: a full round
+# and a reversed partial one of 8, in the four-wave forward (d = 64) and in
+# the dQ pass (both head sizes).
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_serpentine_partial_round_against_full_oracle(d):
+    B, H, N = 5, 8, 1000
+    inp = W.random_inputs(B, H, N, d, "bf16", seed=4242 + d)
+    scale = 1.0 / math.sqrt(d)
+    _say(f"case serpentine B={B} H={H} N={N} d={d} causal")
+    got = run_hip(inp, "bf16", scale, True, None)
+    ref = oracle.forward_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, True, None)
+    check_all(got, ref, "bf16", f"serpentine d={d}")
+
+
+# --------------------------------------------------------------------------
 # Split passes: a shape whose blocks fill few compute units (one head of a
 # long sequence) runs dK/dV as runs of query tiles and dQ as runs of key
 # tiles, each writing fp32 partials that a reduction kernel adds.
